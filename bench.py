@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the SVDQuant W4A4 linear layer on one MI355X.
+
+One step is one full layer call (svdq_linear_w4a4: the fused activation
+kernel, then the W4xA4 GEMM with its low-rank / bias epilogue) on one batch
+of seeded synthetic activations, inputs resident in HBM.  Workload: the
+FLUX-scale projection M 4096 x K 3072 -> N 12288, rank 32, INT4 groups of 64,
+bf16 activations and output.  Weights are quantized once, offline, by the
+library's own svdq_quantize_weights.
+
+Prints one JSON line: TOPS = 2 M N K / (time per step), the roofline of the
+dominant kernel (the GEMM) measured with HIP events on the launch stream, and
+the CPU oracle's throughput on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_FP8_TOPS = 5000.0          # MI355X dense FP8 / INT8 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--nbuf", type=int, default=4, help="distinct X / Y buffers rotated")
+    return ap.parse_args()
+
+
+def gemm_source_sha():
+    h = hashlib.sha256()
+    for f in ("gemm_int4.hip", "internal.h"):
+        with open(os.path.join(ROOT, "w4a4_quantized_diffusion_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(launch_units):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "gemm_int4_flagship_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_sha") != gemm_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(M, K, N, R, seconds):
+    """The oracle forward (INT4 quantization of the activations, exact group
+    products, fp64 scaled accumulation, bf16 low-rank branch) on a bounded
+    sample of rows of the same workload, timed on the host cores."""
+    import numpy as np
+    from oracle import svdq as O
+    from oracle import formats as F
+    from w4a4_quantized_diffusion_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    r = synth.random_int4_layer(N, K, R, seed=0)
+    lay = dict(q=O.unpack_int4(r["wcodes"]), sW=r["sW"], smooth=r["smooth"],
+               lora_down=F.bf16_to_f32(r["lora_down_bits"]).astype(np.float64),
+               lora_up=F.bf16_to_f32(r["lora_up_bits"]).astype(np.float64))
+    x = synth.layer(M, K, 16, 0, seed=0)["x"]
+    rows = 8
+    t = 0.0
+    while True:                      # grow the sample until it is ~1/8 of the budget
+        t0 = time.perf_counter()
+        O.linear_w4a4(x[:rows], lay)
+        t = time.perf_counter() - t0
+        if t > seconds / 8 or rows >= M:
+            break
+        rows = min(M, rows * 2)
+    rows = min(M, max(rows, int(rows * (seconds / max(t, 1e-9)))))
+    t0 = time.perf_counter()
+    O.linear_w4a4(x[:rows], lay)
+    t = time.perf_counter() - t0
+    tops = 2.0 * rows * N * K / t / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} of {M} rows of the same layer (full K={K}, N={N}, rank {R}), "
+                      f"{t:.1f} s, numpy/BLAS on the host"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards "
+              "over tokens with no exchange, so N GPUs would each run this same benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from w4a4_quantized_diffusion_amd import svdq, synth
+
+    M, K, N, R = 4096, 3072, 12288, 32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = synth.layer(M, K, N, R, seed=0, workload="flagship")
+    W = torch.from_numpy(s["w"]).to(dev)
+    xs = [torch.from_numpy(s["x"]).to(dev).to(torch.bfloat16)]
+    for i in range(1, args.nbuf):
+        xs.append(torch.from_numpy(synth.activations(M, K, 0, synth.WORKLOADS["flagship"],
+                                                     10 + i)).to(dev).to(torch.bfloat16))
+    bias = torch.from_numpy(s["b"]).to(dev).to(torch.bfloat16)
+    amax = svdq.svdq_act_absmax(xs[0])
+    layer = svdq.svdq_quantize_weights(W, amax, R, "int4")
+    del W
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(args.nbuf)]
+    ws = torch.empty(svdq.svdq_workspace_bytes(M, K, R), dtype=torch.uint8, device=dev)
+    codes, scales, lr = svdq.workspace_views(ws, M, K, R)
+
+    def step(i):
+        svdq.svdq_linear_w4a4(xs[i % args.nbuf], layer, bias, workspace=ws,
+                              Y=ys[i % args.nbuf])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations, HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        x = xs[i % args.nbuf]
+        evs[i][0].record()
+        svdq.svdq_act_quantize(x, layer, codes, scales, lr)
+        evs[i][1].record()
+        svdq.svdq_gemm_w4a4(codes, scales, lr, layer, bias, Y=ys[i % args.nbuf])
+        evs[i][2].record()
+    torch.cuda.synchronize()
+    t_act = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+
+    ops = 2.0 * M * N * K
+    value = ops / (ms_step * 1e-3) / 1e12
+    gemm_tops = ops / t_gemm.mean() / 1e12
+    act_bytes = M * K * 2 + M * K // 2 + M * (K // 64) * 4 + M * R * 2 + K * 4 + R * K * 2
+    gemm_bytes = (M * K // 2 + M * (K // 64) * 4 + M * R * 2 + N * K // 2 + N * (K // 64) * 4
+                  + N * R * 2 + N * 2 + M * N * 2)
+    traffic = traffic_from_profile(1)
+    out = {
+        "metric": "SVDQ W4A4 linear TOPS & % MFMA peak at M=4096,K=3072,N=12288,r=32",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": "SVDQuant W4A4 linear, INT4 g64, rank 32, M 4096 x K 3072 -> "
+                               "N 12288, bf16 activations / bias / output",
+                   "M": M, "K": K, "N": N, "rank": R, "precision": "int4-g64",
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_mfma_peak": round(100.0 * value / PEAK_FP8_TOPS, 2),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
+        "roofline": {
+            "kernel": "gemm_int4_kernel",
+            "bound": "mfma",
+            "achieved": round(gemm_tops, 2),
+            "peak": PEAK_FP8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tops / PEAK_FP8_TOPS, 4),
+            "traffic": traffic,
+            "algorithmic_ops_per_launch": ops,
+            "algorithmic_bytes_per_launch": gemm_bytes,
+            "avg_launch_us": round(float(t_gemm.mean()) * 1e6, 3),
+        },
+        "kernels": {
+            "act_quant_int4": {"avg_us": round(float(t_act.mean()) * 1e6, 3),
+                               "p95_us": round(float(np.percentile(t_act, 95)) * 1e6, 3),
+                               "algorithmic_bytes": act_bytes,
+                               "GB/s": round(act_bytes / t_act.mean() / 1e9, 1),
+                               "frac_hbm": round(act_bytes / t_act.mean() / 1e9 / PEAK_HBM_GBS, 4)},
+            "gemm_int4": {"avg_us": round(float(t_gemm.mean()) * 1e6, 3),
+                          "p95_us": round(float(np.percentile(t_gemm, 95)) * 1e6, 3),
+                          "TOPS": round(gemm_tops, 2)},
+        },
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(M, K, N, R, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 linear layer.
+ *
+ * The method (pages: "Bringing Nunchaku 4-bit Diffusion Inference to
+ * Diffusers", aiphreaks.com, section "Technical Breakdown and Performance
+ * Metrics"; "Nunchaku Lite: 4-Bit Diffusion-Inferenz direkt in Diffusers",
+ * chaosnode.de, sections "Die Technik: SVDQuant" and "Hardware-Support";
+ * "Nunchaku 4-Bit Diffusion Inference in Diffusers: A Practical Guide",
+ * imaginepro.ai, section "Under the Hood"):
+ *
+ *   - per-channel smoothing moves activation outliers into the weights,
+ *   - the hard part of the smoothed weight is a 16-bit (bf16) rank-r branch,
+ *   - the residual weight and the smoothed activations are quantized to 4 bits
+ *     (INT4 in groups of 64, or NVFP4: FP4-E2M1 in blocks of 16 with E4M3 block
+ *     scales and an fp32 tensor scale),
+ *
+ *     Y = Q4(X * smooth) . Q4(R)^T + bf16(X . lora_down^T) . lora_up^T + b.
+ *
+ * A weight-only layer (awq_w4a16, asymmetric INT4, bf16 scales and zeros) is
+ * the second layer type of the "Hardware-Support" table.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Matrices are row-major.  W is [N, K] (nn.Linear layout: out x in), X is
+ *    [M, K], Y is [M, N].
+ *  - Pointers marked DEVICE are HIP device pointers on the current device;
+ *    the caller owns all of them.  Pointers marked HOST are host memory.
+ *  - Runtime calls (svdq_act_quantize, svdq_gemm_w4a4, svdq_linear_w4a4,
+ *    awq_linear_w4a16) only enqueue kernels on `stream` and return; they
+ *    allocate nothing.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  Offline calls (svdq_quantize_weights,
+ *    awq_quantize_weights) enqueue on `stream`, may allocate temporary
+ *    device memory, and return after their work is complete.
+ *  - Every argument is validated before any HIP call; a bad argument returns
+ *    SVDQ_ERR_INVALID_ARG (nothing is launched), an unsupported combination
+ *    SVDQ_ERR_UNSUPPORTED, a HIP runtime error SVDQ_ERR_HIP.  No call aborts
+ *    or throws.  svdq_last_error() gives a message for the calling thread.
+ *  - Results are deterministic: identical inputs give identical bits.
+ *  - Inputs with NaN or Inf are outside the contract (the output is then
+ *    unspecified, but every kernel still terminates).
+ *
+ * Formats
+ * -------
+ *  bf16 values are passed as uint16_t bit patterns.
+ *  INT4 codes: sign-magnitude nibbles (bit 3 = sign, bits 0..2 = |q|, zero is
+ *  0x0), values -7..7, two per byte, even k in the low nibble; [rows, K/2].
+ *  INT4 group scales: float32 [rows, K/64], scale = fl32(absmax / 7).
+ *  NVFP4 codes: E2M1 nibbles (bit 3 = sign), same packing; block scales are
+ *  E4M3 bytes [rows, K/16]; one float32 tensor scale per tensor.
+ *  AWQ codes: unsigned nibbles 0..15, same packing; scales and zero points
+ *  bf16 [N, K/group].
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARG = 1,
+  SVDQ_ERR_UNSUPPORTED = 2,
+  SVDQ_ERR_HIP = 3
+} svdq_status;
+
+typedef enum { SVDQ_INT4 = 0, SVDQ_NVFP4 = 1 } svdq_precision;
+typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
+
+/* svdq_quantize_weights flag: lora_down / lora_up are INPUTS (the low-rank
+ * split is given, the SVD is skipped); smoothing, residual and quantization
+ * run as usual. */
+#define SVDQ_LOWRANK_GIVEN 1u
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on that thread. */
+const char* svdq_last_error(void);
+
+/* Bytes of the workspace svdq_linear_w4a4 needs for M rows (a multiple of
+ * 256; 0 for invalid arguments).  Layout from the start of the workspace,
+ * each part 256-byte aligned:
+ *   INT4 : A codes u8 [M, K/2], sA f32 [M, K/64], LR bf16 [M, rank]
+ *   NVFP4: A codes u8 [M, K/2], sA E4M3 u8 [M, K/16], LR bf16 [M, rank]  */
+size_t svdq_workspace_bytes(int64_t M, int64_t K, int32_t rank, svdq_precision prec);
+
+/* Byte offsets of the three workspace parts (same layout as above). */
+void svdq_workspace_layout(int64_t M, int64_t K, int32_t rank, svdq_precision prec,
+                           size_t* codes_off, size_t* scales_off, size_t* lr_off);
+
+/* Calibration statistic (smoothing, step 1): amax[k] = max(amax[k],
+ * max_m |X[m, k]|).  X: DEVICE [M, K] of x_dtype.  amax: DEVICE float [K],
+ * read and updated (start from zeros; several calibration batches can be
+ * folded in).  M >= 1, K >= 1. */
+svdq_status svdq_act_absmax(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                            float* amax, hipStream_t stream);
+
+/* Offline weight quantization (steps 1-3 of the method).
+ *
+ *   lam_k    = fl32(sqrt(fl32(act_amax[k] / max_n |W[n,k]|)))  (1 if either is 0)
+ *   smooth_k = fl32(1 / lam_k)                    (act_amax == NULL: lam = 1)
+ *   Wh       = W * lam;  truncated rank-r SVD Wh^T ~= U_r S_r V_r^T
+ *   lora_down[i,k] = bf16(fl32(U_r S_r [k,i] / lam_k)),  lora_up[n,i] = bf16(V_r[n,i])
+ *   R[n,k]   = fl32(Wh[n,k] - lam_k * sum_i lora_up[n,i] lora_down[i,k])
+ *   INT4 : wcodes, wscales (f32 [N, K/64]) = Q4(R)
+ *   NVFP4: ts_w = fl32(max|R| / 2688) (1 if 0); wcodes, wscales (E4M3 u8
+ *          [N, K/16]) = blockwise FP4 of R; ts_x = fl32(max_k fl32(act_amax[k]
+ *          smooth_k) / 2688) (1 if 0), the static activation tensor scale.
+ *
+ * The SVD is computed by block subspace iteration (oversampling 16) with a
+ * Rayleigh-Ritz step; singular vectors are signed so the largest-magnitude
+ * entry of each K-side vector is positive.  Singular subspaces with (near-)
+ * repeated singular values are not unique, so lora_* may differ from another
+ * SVD routine's by such a rotation while L1 L2 is equally close to Wh.
+ *
+ * W: DEVICE f32 [N, K].  act_amax: DEVICE f32 [K] or NULL.
+ * rank: 0 <= rank <= min(N, K).  K % 64 == 0 (INT4) or K % 16 == 0 (NVFP4).
+ * Outputs (DEVICE): smooth f32 [K]; lora_down bf16 [rank, K]; lora_up bf16
+ * [N, rank] (inputs instead when flags has SVDQ_LOWRANK_GIVEN); wcodes u8
+ * [N, K/2]; wscales (see above); w_tensor_scale, x_tensor_scale f32 [1]
+ * (NVFP4 only; may be NULL for INT4); residual f32 [N, K] or NULL.
+ * Temporary device memory is allocated and freed inside the call. */
+svdq_status svdq_quantize_weights(const float* W, int64_t N, int64_t K,
+                                  const float* act_amax, int32_t rank,
+                                  svdq_precision prec, uint32_t flags,
+                                  float* smooth, uint16_t* lora_down, uint16_t* lora_up,
+                                  uint8_t* wcodes, void* wscales,
+                                  float* w_tensor_scale, float* x_tensor_scale,
+                                  float* residual, hipStream_t stream);
+
+/* Runtime activation kernel (step 4): smoothing, per-group quantization with
+ * nibble packing, and the low-rank down-projection, in one pass over X.
+ *   Xh = fl32(X * smooth)
+ *   INT4 : per 64 along K, s = fl32(max|Xh| / 7), q = rne(fl32(Xh / s))
+ *   NVFP4: per 16 along K, sb = E4M3(fl32(max|Xh| / fl32(6 ts_x))),
+ *          q = E2M1(fl32(Xh / fl32(sb ts_x)))
+ *   LR[m, i] = bf16(sum_k bf16(X[m,k]) lora_down[i,k])  (fp32 accumulation)
+ * X: DEVICE [M, K] x_dtype.  smooth f32 [K]; lora_down bf16 [rank, K];
+ * x_tensor_scale DEVICE f32 [1] (NVFP4; ignored for INT4).
+ * Outputs DEVICE: codes u8 [M, K/2]; scales (f32 [M, K/64] or E4M3 u8
+ * [M, K/16]); LR bf16 [M, rank] (rank 0: LR may be NULL).
+ * M >= 0 (0 launches nothing), K % 64 == 0 (INT4) / K % 16 == 0 (NVFP4),
+ * rank % 16 == 0, 0 <= rank <= 256. */
+svdq_status svdq_act_quantize(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                              int32_t rank, svdq_precision prec, const float* smooth,
+                              const uint16_t* lora_down, const float* x_tensor_scale,
+                              uint8_t* codes, void* scales, uint16_t* LR,
+                              hipStream_t stream);
+
+/* Runtime 4-bit GEMM with the fused epilogue (steps 5-6):
+ *   INT4 : Y = sum_g sA[m,g] sW[n,g] I_g[m,n] + LR lora_up^T + bias,
+ *          I_g the exact integer dot product of group g's codes
+ *   NVFP4: Y = ts_x ts_w sum_k xd[m,k] wd[n,k] + LR lora_up^T + bias,
+ *          xd, wd the decoded E2M1 * E4M3 values
+ * Inputs DEVICE: A codes / scales / LR as written by svdq_act_quantize;
+ * wcodes / wscales / lora_up / tensor scales as written by
+ * svdq_quantize_weights; bias [N] of bias_dtype or NULL; Y [M, N] y_dtype.
+ * N % 16 == 0; other constraints as svdq_act_quantize. */
+svdq_status svdq_gemm_w4a4(const uint8_t* codes, const void* scales, const uint16_t* LR,
+                           int64_t M, int64_t K, int64_t N, int32_t rank,
+                           svdq_precision prec, const uint8_t* wcodes, const void* wscales,
+                           const uint16_t* lora_up, const float* w_tensor_scale,
+                           const float* x_tensor_scale, const void* bias,
+                           svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                           hipStream_t stream);
+
+/* The whole layer: svdq_act_quantize into the workspace, then
+ * svdq_gemm_w4a4, on one stream.  bias has x_dtype.  workspace: DEVICE, at
+ * least svdq_workspace_bytes(M, K, rank, prec) bytes, 256-byte aligned, not
+ * overlapping X or Y. */
+svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                             int64_t N, int32_t rank, svdq_precision prec,
+                             const float* smooth, const uint16_t* lora_down,
+                             const uint16_t* lora_up, const uint8_t* wcodes,
+                             const void* wscales, const float* w_tensor_scale,
+                             const float* x_tensor_scale, const void* bias,
+                             void* Y, svdq_dtype y_dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Offline AWQ W4A16 quantization (asymmetric INT4, the awq_w4a16 row of the
+ * "Hardware-Support" table).  Per output row and group of `group` along K:
+ *   mn = min(min w, 0), mx = max(max w, 0), s = bf16(fl32(fl32(mx - mn) / 15))
+ *   s == 0: z = 0, q = 0;  else z = clamp(rne(fl32(-mn / s)), 0, 15),
+ *   q = clamp(rne(fl32(w / s)) + z, 0, 15).
+ * W DEVICE f32 [N, K]; outputs DEVICE q u8 [N, K/2] (unsigned nibbles),
+ * scales, zeros bf16 [N, K/group].  group == 64, K % 64 == 0. */
+svdq_status awq_quantize_weights(const float* W, int64_t N, int64_t K, int32_t group,
+                                 uint8_t* q, uint16_t* scales, uint16_t* zeros,
+                                 hipStream_t stream);
+
+/* AWQ W4A16 linear: Y = X . ((q - z) s)^T + bias, fp32 accumulation with
+ * the group scale applied to the exact per-group sums.
+ * X DEVICE bf16 [M, K]; bias bf16 [N] or NULL; Y [M, N] y_dtype.
+ * M >= 0, N % 16 == 0, group == 64, K % 64 == 0. */
+svdq_status awq_linear_w4a16(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                             int32_t group, const uint8_t* q, const uint16_t* scales,
+                             const uint16_t* zeros, const uint16_t* bias, void* Y,
+                             svdq_dtype y_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVDQ_H */

@@ -1,0 +1,113 @@
+"""Shared helpers of the GPU parity tests: move oracle results and seeded
+inputs to the device, and compare with the documented tolerances."""
+
+import numpy as np
+import torch
+
+from oracle import formats as F
+from oracle import svdq as O
+from w4a4_quantized_diffusion_amd import synth
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def t_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def t_bf16_bits(values):
+    """float values (already bf16-representable or not) -> int16 tensor of
+    their RNE bf16 bit patterns."""
+    bits = F.bf16_bits(np.asarray(values, dtype=np.float64))
+    return torch.from_numpy(bits.view(np.int16).copy()).to(dev())
+
+
+def t_x(x, bf16):
+    """Activations to the device: bf16 tensor (values must be bf16) or fp32."""
+    t = t_f32(x)
+    if bf16:
+        t2 = t.to(torch.bfloat16)
+        assert torch.equal(t2.float(), t), "activation values are not bf16 values"
+        return t2
+    return t
+
+
+def t_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev())
+
+
+def layer_to_device(lay, rank, n, k, prec=0):
+    """An oracle INT4 layer dict -> the binding's device layer dict."""
+    d = dict(rank=rank, prec=prec, N=n, K=k)
+    d["smooth"] = t_f32(lay["smooth"])
+    d["lora_down"] = t_bf16_bits(lay["lora_down"]) if rank else torch.zeros(1, dtype=torch.int16, device=dev())
+    d["lora_up"] = t_bf16_bits(lay["lora_up"]) if rank else torch.zeros(1, dtype=torch.int16, device=dev())
+    d["wcodes"] = t_u8(lay["wcodes"])
+    d["wscales"] = t_f32(lay["sW"])
+    d["w_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev())
+    d["x_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev())
+    return d
+
+
+def random_int4_layer(n, k, rank, seed, workload="flagship"):
+    """The seeded synthetic layer of synth.random_int4_layer in the oracle's
+    dict form (codes unpacked, factors as float64 values)."""
+    r = synth.random_int4_layer(n, k, rank, seed, workload)
+    return dict(q=O.unpack_int4(r["wcodes"]), sW=r["sW"], wcodes=r["wcodes"],
+                smooth=r["smooth"], lora_down=F.bf16_to_f32(r["lora_down_bits"]).astype(np.float64),
+                lora_up=F.bf16_to_f32(r["lora_up_bits"]).astype(np.float64))
+
+
+def bf16_bits_np(t):
+    return t.cpu().numpy().view(np.uint16) if t.dtype == torch.int16 else \
+        t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_ulp_diff(a_bits, b_bits):
+    """Distance in representable steps between two bf16 bit arrays."""
+    def key(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+def assert_lr_close(lr_gpu, x, down, what=""):
+    """LR = bf16(sum_k bf16(X) lora_down) accumulated in fp32 on the GPU:
+    |LR_gpu - exact| <= 2^-8 |exact| (bf16 rounding, which may go either way
+    from a slightly different fp32 sum) + 2 K 2^-24 sum_k |x_k d_k| (a bound
+    on the fp32 summation error in any order).  Where the dot product
+    cancels this is wider than one bf16 step.  Returns the count of entries
+    that are not the oracle's bits."""
+    xb = F.bf16(np.asarray(x, dtype=np.float32))
+    d = np.asarray(down, dtype=np.float64)
+    exact = xb @ d.T
+    sabs = np.abs(xb) @ np.abs(d).T
+    k = xb.shape[1]
+    got = F.bf16_to_f32(bf16_bits_np(lr_gpu)).astype(np.float64)
+    tol = 2.0 ** -8 * np.abs(exact) + 2.0 * k * 2.0 ** -24 * sabs
+    err = np.abs(got - exact)
+    assert np.all(err <= tol), f"{what}: LR out of tolerance at {np.argwhere(err > tol)[:5]}"
+    ref_bits = F.bf16_bits(F.fl32(exact))
+    return int((bf16_bits_np(lr_gpu) != ref_bits).sum())
+
+
+def y_tolerance(y_ref, bf16_out):
+    """max|dY| <= 1e-2 rms(Y); bf16 output adds 2^-8 |Y| per element (the
+    output rounding alone)."""
+    rms = np.sqrt(np.mean(y_ref ** 2))
+    tol = 1e-2 * rms
+    if bf16_out:
+        tol = tol + 2.0 ** -8 * np.abs(y_ref)
+    return tol
+
+
+def assert_y_close(y_gpu, y_ref, bf16_out, what=""):
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    tol = y_tolerance(y_ref, bf16_out)
+    err = np.abs(y - y_ref)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} elements out of tolerance; "
+                           f"max err {err.max():.3e}, rms(Y) {np.sqrt(np.mean(y_ref ** 2)):.3e}")
+    return float(err.max() / np.sqrt(np.mean(y_ref ** 2)))

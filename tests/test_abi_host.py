@@ -1,0 +1,132 @@
+"""Host-side checks of the C-ABI library (no GPU work): it loads, exports every
+entry point the header declares, and rejects bad arguments with the
+documented status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a4_quantized_diffusion_amd import svdq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+INVALID, UNSUPPORTED = 1, 2
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:svdq|awq)_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(svdq.LIB_PATH):
+        pytest.fail("libsvdq.so is not built (run __graft_entry__.build())")
+    return svdq.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("svdq_quantize_weights", "svdq_linear_w4a4", "awq_linear_w4a16",
+              "svdq_act_quantize", "svdq_gemm_w4a4", "awq_quantize_weights"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(svdq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(_declared()) == set(svdq.EXPORTS)
+
+
+def test_workspace_size_and_layout(lib):
+    M, K, r = 4096, 3072, 32
+    n = svdq.svdq_workspace_bytes(M, K, r, "int4")
+    c, s, l = svdq.svdq_workspace_layout(M, K, r, "int4")
+    assert c == 0 and s >= M * K // 2 and l >= s + M * (K // 64) * 4
+    assert n >= l + M * r * 2 and n % 256 == 0 and s % 256 == 0 and l % 256 == 0
+    assert svdq.svdq_workspace_bytes(M, 100, r, "int4") == 0
+    assert svdq.svdq_workspace_bytes(M, K, 17, "int4") == 0
+    nf = svdq.svdq_workspace_bytes(M, K, r, "nvfp4")
+    assert nf >= M * K // 2 + M * K // 16 + M * r * 2
+
+
+@pytest.mark.parametrize("K,rank,msg", [(100, 32, "K must"), (0, 32, "K must"),
+                                        (128, 17, "rank"), (128, -16, "rank"),
+                                        (128, 272, "rank")])
+def test_act_quantize_rejects_bad_shapes(lib, K, rank, msg):
+    st = lib.svdq_act_quantize(None, 1, 64, K, rank, 0, None, None, None, None, None, None, None)
+    assert st == INVALID
+    assert msg in svdq.svdq_last_error()
+
+
+def test_null_pointers_rejected(lib):
+    st = lib.svdq_act_quantize(None, 1, 64, 128, 16, 0, None, None, None, None, None, None, None)
+    assert st == INVALID and "X is NULL" in svdq.svdq_last_error()
+
+
+def test_misaligned_pointer_rejected(lib):
+    st = lib.svdq_act_quantize(ctypes.c_void_p(0x1002), 1, 64, 128, 0, 0, ctypes.c_void_p(0x2000),
+                               None, None, ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000),
+                               None, None)
+    assert st == INVALID and "aligned" in svdq.svdq_last_error()
+
+
+def test_unknown_enums_rejected(lib):
+    assert lib.svdq_act_quantize(None, 7, 64, 128, 16, 0, None, None, None, None, None, None,
+                                 None) == INVALID
+    assert lib.svdq_act_quantize(None, 1, 64, 128, 16, 5, None, None, None, None, None, None,
+                                 None) == INVALID
+
+
+def test_gemm_rejects_bad_n(lib):
+    st = lib.svdq_gemm_w4a4(None, None, None, 64, 128, 100, 16, 0, None, None, None, None, None,
+                            None, 0, None, 0, None)
+    assert st == INVALID and "N must" in svdq.svdq_last_error()
+
+
+def test_linear_rejects_small_workspace(lib):
+    p = ctypes.c_void_p
+    st = lib.svdq_linear_w4a4(p(0x10000), 1, 64, 128, 64, 16, 0, p(0x20000), p(0x30000),
+                              p(0x40000), p(0x50000), p(0x60000), None, None, None,
+                              p(0x70000), 0, p(0x100000), 100, None)
+    assert st == INVALID and "workspace too small" in svdq.svdq_last_error()
+
+
+def test_linear_rejects_overlap(lib):
+    p = ctypes.c_void_p
+    need = svdq.svdq_workspace_bytes(64, 128, 16, "int4")
+    st = lib.svdq_linear_w4a4(p(0x100000), 1, 64, 128, 64, 16, 0, p(0x20000), p(0x30000),
+                              p(0x40000), p(0x50000), p(0x60000), None, None, None,
+                              p(0x900000), 0, p(0x100000), need, None)
+    assert st == INVALID and "overlap" in svdq.svdq_last_error()
+
+
+def test_quantize_weights_rejects_rank(lib):
+    st = lib.svdq_quantize_weights(ctypes.c_void_p(0x1000), 32, 64, None, 48, 0, 0,
+                                   *([None] * 9))
+    assert st == INVALID and "rank" in svdq.svdq_last_error()
+
+
+def test_quantize_weights_rejects_flags(lib):
+    st = lib.svdq_quantize_weights(ctypes.c_void_p(0x1000), 32, 64, None, 16, 0, 8,
+                                   *([None] * 9))
+    assert st == INVALID and "flags" in svdq.svdq_last_error()
+
+
+def test_awq_rejects_group(lib):
+    assert lib.awq_linear_w4a16(None, 1, 128, 64, 128, None, None, None, None, None, 1,
+                                None) == UNSUPPORTED
+    assert lib.awq_quantize_weights(None, 64, 128, 32, None, None, None, None) == UNSUPPORTED
+
+
+def test_zero_rows_is_a_noop(lib):
+    # M == 0: valid, nothing launched, no pointer needed
+    assert lib.svdq_act_quantize(None, 1, 0, 128, 16, 0, None, None, None, None, None, None,
+                                 None) == 0
+    assert lib.awq_linear_w4a16(None, 0, 128, 64, 64, None, None, None, None, None, 1,
+                                None) == 0

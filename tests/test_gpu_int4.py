@@ -1,0 +1,204 @@
+"""GPU parity of the INT4 SVDQuant path against the CPU oracle, through the
+C ABI: activation codes / scales bit-exact, LR within one bf16 step, exact
+integer group sums (unit-scale mode), Y within 1e-2 rms(Y), the offline
+quantizer's smoothing / residual / codes bit-exact for a given low-rank
+split, and full-size runs in the benchmark's launch configuration checked on
+sampled rows."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import svdq as O
+from oracle import formats as F
+from w4a4_quantized_diffusion_amd import svdq, synth
+from tests.gpu_helpers import (t_f32, t_x, t_u8, t_bf16_bits, layer_to_device,
+                               random_int4_layer, bf16_bits_np, assert_lr_close, assert_y_close)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_layer(w, x, rank):
+    return O.quantize_weights(w, O.act_absmax(x), rank)
+
+
+def _check_act(x_np, lay, rank, bf16):
+    m, k = x_np.shape
+    d = layer_to_device(lay, rank, lay["q"].shape[0], k)
+    codes, scales, lr = svdq.svdq_act_quantize(t_x(x_np, bf16), d)
+    torch.cuda.synchronize()
+    qx, sa = O.quantize_activations(x_np, lay["smooth"])
+    assert np.array_equal(codes.cpu().numpy(), O.pack_int4(qx)), "activation codes differ"
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), sa.view(np.uint32)), "scales differ"
+    if rank:
+        mism = assert_lr_close(lr, x_np, lay["lora_down"], "LR")
+        assert mism <= 0.01 * lr.numel(), f"{mism} LR entries differ from the oracle's bits"
+        return mism
+    return 0
+
+
+def test_act_quant_small_workload_fp32():
+    s = synth.small()
+    lay = _oracle_layer(s["w"], s["x"], s["rank"])
+    _check_act(s["x"], lay, s["rank"], bf16=False)
+
+
+@pytest.mark.parametrize("m", [1, 100, 257])
+def test_act_quant_bf16_ragged_rows(m):
+    s = synth.layer(m, 3072, 256, 32, seed=1, workload="attn")
+    lay = _oracle_layer(s["w"], s["x"], 32)
+    _check_act(s["x"], lay, 32, bf16=True)
+
+
+def test_gemm_unit_scale_exact_integers():
+    """rank 0, all scales 1, no bias, fp32 out: Y is the exact integer dot
+    product of the codes (below 2^24, so exact in fp32)."""
+    g = np.random.default_rng(7)
+    m, k, n = 130, 320, 208
+    qx = g.integers(-7, 8, (m, k)).astype(np.int8)
+    qw = g.integers(-7, 8, (n, k)).astype(np.int8)
+    qx[0, :] = 7
+    qw[0, :] = -7                                    # extreme sums -49*k
+    ones_a = torch.ones((m, k // 64), dtype=torch.float32, device="cuda")
+    lay = dict(rank=0, prec=0, N=n, K=k, wcodes=t_u8(O.pack_int4(qw)),
+               wscales=torch.ones((n, k // 64), dtype=torch.float32, device="cuda"),
+               lora_up=None, w_tensor_scale=None, x_tensor_scale=None)
+    y = svdq.svdq_gemm_w4a4(t_u8(O.pack_int4(qx)), ones_a, None, lay)
+    ref = sum(O.group_int_products(qx, qw, gi) for gi in range(k // 64))
+    assert np.array_equal(y.cpu().numpy(), ref.astype(np.float32))
+
+
+def test_gemm_single_nonzero_group():
+    """Only group 2 non-zero, per-row/column power-of-two scales: the output is
+    exactly sA sW I_2."""
+    g = np.random.default_rng(8)
+    m, k, n = 64, 256, 64
+    qx = np.zeros((m, k), np.int8)
+    qw = np.zeros((n, k), np.int8)
+    qx[:, 128:192] = g.integers(-7, 8, (m, 64))
+    qw[:, 128:192] = g.integers(-7, 8, (n, 64))
+    sa = np.ldexp(1.0, g.integers(-8, 8, (m, k // 64))).astype(np.float32)
+    sw = np.ldexp(1.0, g.integers(-8, 8, (n, k // 64))).astype(np.float32)
+    lay = dict(rank=0, prec=0, N=n, K=k, wcodes=t_u8(O.pack_int4(qw)), wscales=t_f32(sw),
+               lora_up=None, w_tensor_scale=None, x_tensor_scale=None)
+    y = svdq.svdq_gemm_w4a4(t_u8(O.pack_int4(qx)), t_f32(sa), None, lay)
+    ref = sa[:, 2:3].astype(np.float64) * sw[:, 2].astype(np.float64)[None, :] * \
+        O.group_int_products(qx, qw, 2)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("ybf16", [False, True])
+def test_linear_small_workload(ybf16):
+    s = synth.small()
+    lay = _oracle_layer(s["w"], s["x"], s["rank"])
+    d = layer_to_device(lay, s["rank"], 1024, 1024)
+    y = svdq.svdq_linear_w4a4(t_x(s["x"], False), d, bias=t_f32(s["b"]),
+                              y_dtype=torch.bfloat16 if ybf16 else torch.float32)
+    y_ref, _ = O.linear_w4a4(s["x"], lay, s["b"])
+    assert_y_close(y, y_ref, ybf16, "small workload")
+
+
+@pytest.mark.parametrize("m,k,n,rank", [(77, 192, 48, 16), (300, 1024, 272, 32),
+                                        (129, 640, 144, 0), (5, 3072, 400, 48)])
+def test_linear_ragged_shapes(m, k, n, rank):
+    s = synth.layer(m, k, n, rank, seed=3, workload="attn")
+    lay = _oracle_layer(s["w"], s["x"], rank)
+    d = layer_to_device(lay, rank, n, k)
+    bias = torch.from_numpy(s["b"]).to("cuda").to(torch.bfloat16)
+    y = svdq.svdq_linear_w4a4(t_x(s["x"], True), d, bias=bias)
+    y_ref, _ = O.linear_w4a4(s["x"], lay, s["b"])
+    assert_y_close(y, y_ref, False, f"{m}x{k}x{n} r{rank}")
+
+
+def test_linear_deterministic_and_fully_written():
+    s = synth.layer(200, 1024, 336, 32, seed=4, workload="attn")
+    lay = _oracle_layer(s["w"], s["x"], 32)
+    d = layer_to_device(lay, 32, 336, 1024)
+    x = t_x(s["x"], True)
+    buf = torch.full((200 * 336 + 4096,), float("nan"), dtype=torch.float32, device="cuda")
+    y1 = buf[:200 * 336].view(200, 336)
+    svdq.svdq_linear_w4a4(x, d, Y=y1)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y1).any(), "unwritten output elements"
+    assert torch.isnan(buf[200 * 336:]).all(), "write past the end of Y"
+    y2 = svdq.svdq_linear_w4a4(x, d)
+    assert torch.equal(y1, y2), "two runs differ"
+
+
+def test_act_absmax_matches():
+    s = synth.layer(333, 1024, 16, 0, seed=5, workload="attn")
+    a = svdq.svdq_act_absmax(t_x(s["x"], True))
+    assert np.array_equal(a.cpu().numpy(), O.act_absmax(s["x"]))
+    x2 = synth.layer(50, 1024, 16, 0, seed=6, workload="attn")["x"]
+    a = svdq.svdq_act_absmax(t_x(x2, True), a)
+    assert np.array_equal(a.cpu().numpy(), np.maximum(O.act_absmax(s["x"]), O.act_absmax(x2)))
+
+
+# ------------------------------------------------------- offline quantizer
+
+def test_quantize_weights_given_lowrank_bit_exact():
+    s = synth.small()
+    amax = O.act_absmax(s["x"])
+    lay = O.quantize_weights(s["w"], amax, s["rank"])
+    out = svdq.svdq_quantize_weights(
+        t_f32(s["w"]), t_f32(amax), s["rank"], "int4",
+        lowrank=(t_bf16_bits(lay["lora_down"]), t_bf16_bits(lay["lora_up"])), residual=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["smooth"].cpu().numpy(), lay["smooth"]), "smooth differs"
+    assert np.array_equal(out["residual"].cpu().numpy().view(np.uint32), lay["R"].view(np.uint32)), \
+        "residual differs"
+    assert np.array_equal(out["wcodes"].cpu().numpy(), lay["wcodes"]), "weight codes differ"
+    assert np.array_equal(out["wscales"].cpu().numpy(), lay["sW"]), "weight scales differ"
+
+
+def test_quantize_weights_svd_quality():
+    """The library's own SVD: its low-rank split is as good as LAPACK's
+    (Frobenius error of the rank-r part within 1e-3 of Eckart-Young), and the
+    residual / codes it returns satisfy the quantizer's properties."""
+    s = synth.small()
+    amax = O.act_absmax(s["x"])
+    out = svdq.svdq_quantize_weights(t_f32(s["w"]), t_f32(amax), s["rank"], "int4", residual=True)
+    torch.cuda.synchronize()
+    lam, smooth = O.smoothing(amax, s["w"])
+    wh = s["w"].astype(np.float64) * lam.astype(np.float64)[None, :]
+    _, _, sv = O.truncated_svd(wh, s["rank"])
+    ey = np.sum(sv[s["rank"]:] ** 2)
+    down = F.bf16_to_f32(bf16_bits_np(out["lora_down"])).astype(np.float64)
+    up = F.bf16_to_f32(bf16_bits_np(out["lora_up"])).astype(np.float64)
+    low = lam.astype(np.float64)[None, :] * (up @ down)
+    err = np.sum((wh - low) ** 2)
+    ref = O.quantize_weights(s["w"], amax, s["rank"])
+    err_ref = np.sum((wh - lam.astype(np.float64)[None, :] * (ref["lora_up"] @ ref["lora_down"])) ** 2)
+    # bf16 rounding of the factors adds the same kind of error to both
+    assert err <= err_ref * (1 + 1e-3) + 1e-3 * ey, (err, err_ref, ey)
+    # residual identity and quantizer properties on the library's own output
+    r = out["residual"].cpu().numpy()
+    assert np.allclose(wh - low, r, rtol=0, atol=np.abs(r).max() * 2 ** -22 + 1e-30)
+    q = O.unpack_int4(out["wcodes"].cpu().numpy()).astype(np.float64)
+    sw = np.repeat(out["wscales"].cpu().numpy().astype(np.float64), 64, axis=1)
+    assert np.all(np.abs(r - sw * q) <= 0.5 * sw * (1 + 2 ** -22))
+
+
+# ------------------------------------------------------------ full size
+
+def test_flagship_full_size_sampled_rows():
+    """M 4096, K 3072, N 12288, rank 32 (the benchmark's configuration):
+    activation codes / scales bit-exact on every row, Y on sampled rows."""
+    m, k, n, rank = 4096, 3072, 12288, 32
+    x = synth.layer(m, k, 16, 0, seed=0)["x"]
+    lay = random_int4_layer(n, k, rank, seed=0)
+    d = layer_to_device(lay, rank, n, k)
+    xt = t_x(x, True)
+    need = svdq.svdq_workspace_bytes(m, k, rank)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y = svdq.svdq_linear_w4a4(xt, d, workspace=ws, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    codes, scales, lr = svdq.workspace_views(ws, m, k, rank)
+    qx, sa = O.quantize_activations(x, lay["smooth"])
+    assert np.array_equal(codes.cpu().numpy(), O.pack_int4(qx))
+    assert np.array_equal(scales.cpu().numpy(), sa)
+    rows = np.random.default_rng(0).choice(m, 24, replace=False)
+    rows = np.concatenate([rows, [0, m - 1]])
+    y_ref, _ = O.linear_w4a4(x[rows], lay)
+    assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, "flagship rows")
+    assert_lr_close(lr[torch.from_numpy(rows).cuda()], x[rows], lay["lora_down"], "flagship LR")

@@ -97,3 +97,24 @@ def calibration(m, k, seed=0, workload="flagship"):
 def random_bytes(shape, seed, workload, tensor):
     g = rng(seed, workload, tensor)
     return g.integers(0, 256, size=shape, dtype=np.uint8)
+
+
+def random_int4_layer(n, k, rank, seed=0, workload="flagship"):
+    """A quantized INT4 layer drawn directly (no SVD), for runtime tests and
+    timing at full size.  Codes are uniform on -7..7 in the packed
+    sign-magnitude nibble format (two per byte, even k low); weight scales,
+    smoothing factors and low-rank factors are positive / Gaussian draws, the
+    factors rounded to bf16.  Returns numpy arrays: wcodes u8 [n, k/2],
+    sW f32 [n, k/64], smooth f32 [k], lora_down / lora_up bf16 bit patterns
+    (uint16) [rank, k] / [n, rank]."""
+    w = WORKLOADS[workload]
+    g = rng(seed, w, 900)
+    mag = g.integers(0, 8, size=(n, k), dtype=np.uint8)
+    neg = (g.integers(0, 2, size=(n, k), dtype=np.uint8) == 1) & (mag != 0)
+    nib = mag | (neg.astype(np.uint8) << 3)
+    wcodes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    sw = (g.uniform(0.5, 2.0, size=(n, k // 64)) * 2e-3).astype(np.float32)
+    smooth = g.uniform(0.05, 0.5, size=k).astype(np.float32)
+    down = to_bf16_bits(round_bf16((g.standard_normal((rank, k)) * 0.05).astype(np.float32)))
+    up = to_bf16_bits(round_bf16((g.standard_normal((n, rank)) * 0.02).astype(np.float32)))
+    return dict(wcodes=wcodes, sW=sw, smooth=smooth, lora_down_bits=down, lora_up_bits=up)
