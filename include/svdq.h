@@ -43,8 +43,12 @@
  * -------
  *  bf16 values are passed as uint16_t bit patterns.
  *  INT4 codes: sign-magnitude nibbles (bit 3 = sign, bits 0..2 = |q|, zero is
- *  0x0), values -7..7, two per byte, even k in the low nibble; [rows, K/2].
- *  INT4 group scales: float32 [rows, K/64], scale = fl32(absmax / 7).
+ *  0x0), values -7..7, two per byte, even k in the low nibble.  Group-major
+ *  layout [K/64][rows][32 bytes]: the 64 codes of (group g, row r) are the 32
+ *  bytes at offset (g * rows + r) * 32, so a GEMM tile's loads of one group
+ *  are contiguous.
+ *  INT4 group scales: float32, group-major [K/64][rows], scale =
+ *  fl32(absmax / 7).
  *  NVFP4 codes: E2M1 nibbles (bit 3 = sign), same packing; block scales are
  *  E4M3 bytes [rows, K/16]; one float32 tensor scale per tensor.
  *  AWQ codes: unsigned nibbles 0..15, same packing; scales and zero points
@@ -83,7 +87,7 @@ const char* svdq_last_error(void);
 /* Bytes of the workspace svdq_linear_w4a4 needs for M rows (a multiple of
  * 256; 0 for invalid arguments).  Layout from the start of the workspace,
  * each part 256-byte aligned:
- *   INT4 : A codes u8 [M, K/2], sA f32 [M, K/64], LR bf16 [M, rank]
+ *   INT4 : A codes [K/64][M][32] bytes, sA f32 [K/64][M], LR bf16 [M, rank]
  *   NVFP4: A codes u8 [M, K/2], sA E4M3 u8 [M, K/16], LR bf16 [M, rank]  */
 size_t svdq_workspace_bytes(int64_t M, int64_t K, int32_t rank, svdq_precision prec);
 
@@ -105,7 +109,7 @@ svdq_status svdq_act_absmax(const void* X, svdq_dtype x_dtype, int64_t M, int64_
  *   Wh       = W * lam;  truncated rank-r SVD Wh^T ~= U_r S_r V_r^T
  *   lora_down[i,k] = bf16(fl32(U_r S_r [k,i] / lam_k)),  lora_up[n,i] = bf16(V_r[n,i])
  *   R[n,k]   = fl32(Wh[n,k] - lam_k * sum_i lora_up[n,i] lora_down[i,k])
- *   INT4 : wcodes, wscales (f32 [N, K/64]) = Q4(R)
+ *   INT4 : wcodes, wscales (f32 [K/64][N]) = Q4(R)
  *   NVFP4: ts_w = fl32(max|R| / 2688) (1 if 0); wcodes, wscales (E4M3 u8
  *          [N, K/16]) = blockwise FP4 of R; ts_x = fl32(max_k fl32(act_amax[k]
  *          smooth_k) / 2688) (1 if 0), the static activation tensor scale.
@@ -117,10 +121,11 @@ svdq_status svdq_act_absmax(const void* X, svdq_dtype x_dtype, int64_t M, int64_
  * SVD routine's by such a rotation while L1 L2 is equally close to Wh.
  *
  * W: DEVICE f32 [N, K].  act_amax: DEVICE f32 [K] or NULL.
- * rank: 0 <= rank <= min(N, K).  K % 64 == 0 (INT4) or K % 16 == 0 (NVFP4).
+ * rank: 0 <= rank <= min(N, K).  K % 64 == 0.
  * Outputs (DEVICE): smooth f32 [K]; lora_down bf16 [rank, K]; lora_up bf16
  * [N, rank] (inputs instead when flags has SVDQ_LOWRANK_GIVEN); wcodes u8
- * [N, K/2]; wscales (see above); w_tensor_scale, x_tensor_scale f32 [1]
+ * N*K/2 bytes (INT4: group-major [K/64][N][32]; NVFP4: [N, K/2]); wscales
+ * (INT4: f32 [K/64][N]; NVFP4: E4M3 u8 [N, K/16]); w_tensor_scale, x_tensor_scale f32 [1]
  * (NVFP4 only; may be NULL for INT4); residual f32 [N, K] or NULL.
  * Temporary device memory is allocated and freed inside the call. */
 svdq_status svdq_quantize_weights(const float* W, int64_t N, int64_t K,
@@ -140,8 +145,9 @@ svdq_status svdq_quantize_weights(const float* W, int64_t N, int64_t K,
  *   LR[m, i] = bf16(sum_k bf16(X[m,k]) lora_down[i,k])  (fp32 accumulation)
  * X: DEVICE [M, K] x_dtype.  smooth f32 [K]; lora_down bf16 [rank, K];
  * x_tensor_scale DEVICE f32 [1] (NVFP4; ignored for INT4).
- * Outputs DEVICE: codes u8 [M, K/2]; scales (f32 [M, K/64] or E4M3 u8
- * [M, K/16]); LR bf16 [M, rank] (rank 0: LR may be NULL).
+ * Outputs DEVICE: codes M*K/2 bytes (INT4: group-major [K/64][M][32]; NVFP4:
+ * [M, K/2]); scales (INT4: f32 [K/64][M]; NVFP4: E4M3 u8 [M, K/16]); LR bf16
+ * [M, rank] (rank 0: LR may be NULL).
  * M >= 0 (0 launches nothing), K % 64 == 0 (INT4) / K % 16 == 0 (NVFP4),
  * rank % 16 == 0, 0 <= rank <= 256. */
 svdq_status svdq_act_quantize(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,

@@ -38,14 +38,32 @@ def t_u8(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev())
 
 
+def gm_codes(packed):
+    """Row-major packed codes [rows, K/2] -> group-major [K/64, rows, 32]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows, half = packed.shape
+    return np.ascontiguousarray(packed.reshape(rows, half // 32, 32).transpose(1, 0, 2))
+
+
+def rm_codes(gm):
+    """Group-major [K/64, rows, 32] -> row-major [rows, K/2]."""
+    gm = np.asarray(gm, dtype=np.uint8)
+    g, rows, _ = gm.shape
+    return np.ascontiguousarray(gm.transpose(1, 0, 2).reshape(rows, g * 32))
+
+
+def gm_scales(s):
+    return np.ascontiguousarray(np.asarray(s).T)
+
+
 def layer_to_device(lay, rank, n, k, prec=0):
     """An oracle INT4 layer dict -> the binding's device layer dict."""
     d = dict(rank=rank, prec=prec, N=n, K=k)
     d["smooth"] = t_f32(lay["smooth"])
     d["lora_down"] = t_bf16_bits(lay["lora_down"]) if rank else torch.zeros(1, dtype=torch.int16, device=dev())
     d["lora_up"] = t_bf16_bits(lay["lora_up"]) if rank else torch.zeros(1, dtype=torch.int16, device=dev())
-    d["wcodes"] = t_u8(lay["wcodes"])
-    d["wscales"] = t_f32(lay["sW"])
+    d["wcodes"] = t_u8(gm_codes(lay["wcodes"]))
+    d["wscales"] = t_f32(gm_scales(lay["sW"]))
     d["w_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev())
     d["x_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev())
     return d

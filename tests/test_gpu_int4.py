@@ -13,7 +13,8 @@ from oracle import svdq as O
 from oracle import formats as F
 from w4a4_quantized_diffusion_amd import svdq, synth
 from tests.gpu_helpers import (t_f32, t_x, t_u8, t_bf16_bits, layer_to_device,
-                               random_int4_layer, bf16_bits_np, assert_lr_close, assert_y_close)
+                               random_int4_layer, bf16_bits_np, assert_lr_close, assert_y_close,
+                               gm_codes, rm_codes, gm_scales)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,8 +29,8 @@ def _check_act(x_np, lay, rank, bf16):
     codes, scales, lr = svdq.svdq_act_quantize(t_x(x_np, bf16), d)
     torch.cuda.synchronize()
     qx, sa = O.quantize_activations(x_np, lay["smooth"])
-    assert np.array_equal(codes.cpu().numpy(), O.pack_int4(qx)), "activation codes differ"
-    assert np.array_equal(scales.cpu().numpy().view(np.uint32), sa.view(np.uint32)), "scales differ"
+    assert np.array_equal(rm_codes(codes.cpu().numpy()), O.pack_int4(qx)), "activation codes differ"
+    assert np.array_equal(scales.cpu().numpy().T.view(np.uint32), sa.view(np.uint32)), "scales differ"
     if rank:
         mism = assert_lr_close(lr, x_np, lay["lora_down"], "LR")
         assert mism <= 0.01 * lr.numel(), f"{mism} LR entries differ from the oracle's bits"
@@ -59,11 +60,11 @@ def test_gemm_unit_scale_exact_integers():
     qw = g.integers(-7, 8, (n, k)).astype(np.int8)
     qx[0, :] = 7
     qw[0, :] = -7                                    # extreme sums -49*k
-    ones_a = torch.ones((m, k // 64), dtype=torch.float32, device="cuda")
-    lay = dict(rank=0, prec=0, N=n, K=k, wcodes=t_u8(O.pack_int4(qw)),
-               wscales=torch.ones((n, k // 64), dtype=torch.float32, device="cuda"),
+    ones_a = torch.ones((k // 64, m), dtype=torch.float32, device="cuda")
+    lay = dict(rank=0, prec=0, N=n, K=k, wcodes=t_u8(gm_codes(O.pack_int4(qw))),
+               wscales=torch.ones((k // 64, n), dtype=torch.float32, device="cuda"),
                lora_up=None, w_tensor_scale=None, x_tensor_scale=None)
-    y = svdq.svdq_gemm_w4a4(t_u8(O.pack_int4(qx)), ones_a, None, lay)
+    y = svdq.svdq_gemm_w4a4(t_u8(gm_codes(O.pack_int4(qx))), ones_a, None, lay)
     ref = sum(O.group_int_products(qx, qw, gi) for gi in range(k // 64))
     assert np.array_equal(y.cpu().numpy(), ref.astype(np.float32))
 
@@ -79,9 +80,10 @@ def test_gemm_single_nonzero_group():
     qw[:, 128:192] = g.integers(-7, 8, (n, 64))
     sa = np.ldexp(1.0, g.integers(-8, 8, (m, k // 64))).astype(np.float32)
     sw = np.ldexp(1.0, g.integers(-8, 8, (n, k // 64))).astype(np.float32)
-    lay = dict(rank=0, prec=0, N=n, K=k, wcodes=t_u8(O.pack_int4(qw)), wscales=t_f32(sw),
-               lora_up=None, w_tensor_scale=None, x_tensor_scale=None)
-    y = svdq.svdq_gemm_w4a4(t_u8(O.pack_int4(qx)), t_f32(sa), None, lay)
+    lay = dict(rank=0, prec=0, N=n, K=k, wcodes=t_u8(gm_codes(O.pack_int4(qw))),
+               wscales=t_f32(gm_scales(sw)), lora_up=None, w_tensor_scale=None,
+               x_tensor_scale=None)
+    y = svdq.svdq_gemm_w4a4(t_u8(gm_codes(O.pack_int4(qx))), t_f32(gm_scales(sa)), None, lay)
     ref = sa[:, 2:3].astype(np.float64) * sw[:, 2].astype(np.float64)[None, :] * \
         O.group_int_products(qx, qw, 2)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
@@ -147,8 +149,8 @@ def test_quantize_weights_given_lowrank_bit_exact():
     assert np.array_equal(out["smooth"].cpu().numpy(), lay["smooth"]), "smooth differs"
     assert np.array_equal(out["residual"].cpu().numpy().view(np.uint32), lay["R"].view(np.uint32)), \
         "residual differs"
-    assert np.array_equal(out["wcodes"].cpu().numpy(), lay["wcodes"]), "weight codes differ"
-    assert np.array_equal(out["wscales"].cpu().numpy(), lay["sW"]), "weight scales differ"
+    assert np.array_equal(rm_codes(out["wcodes"].cpu().numpy()), lay["wcodes"]), "weight codes differ"
+    assert np.array_equal(out["wscales"].cpu().numpy().T, lay["sW"]), "weight scales differ"
 
 
 def test_quantize_weights_svd_quality():
@@ -174,8 +176,8 @@ def test_quantize_weights_svd_quality():
     # residual identity and quantizer properties on the library's own output
     r = out["residual"].cpu().numpy()
     assert np.allclose(wh - low, r, rtol=0, atol=np.abs(r).max() * 2 ** -22 + 1e-30)
-    q = O.unpack_int4(out["wcodes"].cpu().numpy()).astype(np.float64)
-    sw = np.repeat(out["wscales"].cpu().numpy().astype(np.float64), 64, axis=1)
+    q = O.unpack_int4(rm_codes(out["wcodes"].cpu().numpy())).astype(np.float64)
+    sw = np.repeat(out["wscales"].cpu().numpy().T.astype(np.float64), 64, axis=1)
     assert np.all(np.abs(r - sw * q) <= 0.5 * sw * (1 + 2 ** -22))
 
 
@@ -195,8 +197,8 @@ def test_flagship_full_size_sampled_rows():
     torch.cuda.synchronize()
     codes, scales, lr = svdq.workspace_views(ws, m, k, rank)
     qx, sa = O.quantize_activations(x, lay["smooth"])
-    assert np.array_equal(codes.cpu().numpy(), O.pack_int4(qx))
-    assert np.array_equal(scales.cpu().numpy(), sa)
+    assert np.array_equal(rm_codes(codes.cpu().numpy()), O.pack_int4(qx))
+    assert np.array_equal(scales.cpu().numpy().T, sa)
     rows = np.random.default_rng(0).choice(m, 24, replace=False)
     rows = np.concatenate([rows, [0, m - 1]])
     y_ref, _ = O.linear_w4a4(x[rows], lay)

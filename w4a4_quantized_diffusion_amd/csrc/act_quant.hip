@@ -9,6 +9,9 @@
 //   per block: E4M3 block scale, E2M1 codes      (NVFP4, blocks of 16)
 //   LR = bf16(X) . lora_down^T                   (low-rank down-projection)
 //
+// Output layout (INT4): group-major, codes[K/64][M][32 bytes] and
+// scales[K/64][M]; NVFP4 keeps row-major codes[M][K/2], scales[M][K/16].
+//
 // Work split: a workgroup of 4 waves owns 16 rows; wave w takes the K-groups
 // w, w+4, ... so that at every step the 4 waves read adjacent 128-byte
 // pieces of each row.  Lane l owns row (l % 16) and the two 8-element
@@ -163,10 +166,12 @@ __global__ __launch_bounds__(256) void act_quant_int4_kernel(
       }
     }
     if (ok) {
-      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + row * (K / 2));
-      cp[k0 / 8] = w0;
-      cp[k1 / 8] = w1;
-      if (q == 0) scales[row * G + g] = s;
+      // group-major layout: the 32 bytes of (group g, row) follow those of
+      // (g, row - 1), so the GEMM's loads of a group are contiguous
+      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + (int64_t(g) * M + row) * 32);
+      cp[q] = w0;
+      cp[4 + q] = w1;
+      if (q == 0) scales[int64_t(g) * M + row] = s;
     }
     lr_mfma<RB>(acc, b0, down, K, r, k0);
     lr_mfma<RB>(acc, b1, down, K, r, k1);

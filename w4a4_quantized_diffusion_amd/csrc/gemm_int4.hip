@@ -31,6 +31,8 @@
 
 #include "internal.h"
 
+#include <cstddef>
+
 using namespace svdq_dev;
 
 namespace {
@@ -62,18 +64,56 @@ __device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32
 }
 
 // --------------------------------------------------------------- tiling
+//
+// Workgroup tile 256 x 256, 8 waves (2 per SIMD) arranged 2 (M) x 4 (N), each
+// wave 128 x 64 = 4 x 2 blocks of 32 x 32 (128 fp32 accumulators per lane,
+// in VGPRs so the vector ALU can apply the group scales).  One K-group (64
+// codes) per pipeline step: while the waves run the MFMAs of group g out of
+// one LDS buffer, they widen the packed codes of group g+1 (already in
+// registers) into the other buffer and issue the global loads of group g+2.
+// One barrier per group.  LDS rows are padded to 80 bytes so that the 16
+// lanes of one ds_read_b128 phase (16 consecutive rows) hit distinct banks.
 
-constexpr int BM = 128, BN = 128;       // workgroup tile
-constexpr int NT = 256;                 // 4 waves: 2 x 2, each 64 x 64
-constexpr int ROWB = 64;                // LDS bytes per row and group
-constexpr int LDS_ROW = ROWB + 16;      // padded row pitch (bank spread)
+constexpr int BM = 256, BN = 256;
+constexpr int NT = 512;
+constexpr int WM = 128, WN = 64;        // wave tile
+constexpr int RBL = WM / 32, CBL = WN / 32;
+constexpr int LDS_ROW = 80;             // 64 bytes of E4M3 codes + 16 pad
 
-struct Smem {
+struct Stage {
   uint8_t a[BM * LDS_ROW];
   uint8_t b[BN * LDS_ROW];
-  uint32_t sa[BM][4];                   // S-MFMA A operand pieces per row
-  uint32_t sb[BN][4];
+  uint4 sa[2][BM];                      // scale pieces, A operand, per k-slot half
+  uint4 sb[2][BN];                      // scale pieces, B operand, per k-slot half
 };
+
+// Packed codes and scales of one group, fetched global -> LDS by DMA.  Each
+// wave fetches the 64 rows it stages: 2 KB of codes in two contiguous 1 KB
+// transfers (lane L lands at base + 16 L), so row r of the wave sits at
+// code[wave][32 r], and the 64 scales in one transfer.
+struct Packed {
+  uint8_t code[NT / 64][64 * 32];
+  float scale[NT];
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+// LDS stores at a compile-time byte offset from one address register
+template <int OFF>
+__device__ __forceinline__ void lds_store_b64(uint32_t addr, v2i_t d) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_store_b128(uint32_t addr, v4i d) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF));
+}
+__device__ __forceinline__ v2i_t widen8(uint32_t word) {
+  uint32_t lo, hi;
+  nib8_to_e4m3(word, lo, hi);
+  return v2i_t{int(lo), int(hi)};
+}
 
 template <typename T>
 __device__ __forceinline__ float load_bias(const void* p, int64_t n);
@@ -86,137 +126,312 @@ __device__ __forceinline__ float load_bias<uint16_t>(const void* p, int64_t n) {
   return bf16_to_f32(static_cast<const uint16_t*>(p)[n]);
 }
 
+__device__ __forceinline__ v8i lds_frag(const uint8_t* base) {
+  const uint4 x = reinterpret_cast<const uint4*>(base)[0];
+  const uint4 y = reinterpret_cast<const uint4*>(base)[1];
+  return v8i{int(x.x), int(x.y), int(x.z), int(x.w), int(y.x), int(y.y), int(y.z), int(y.w)};
+}
+
+// Widen 32 packed bytes (64 nibbles) into 64 E4M3 bytes in an LDS row.
+__device__ __forceinline__ void unpack_row(const uint4& p0, const uint4& p1, uint8_t* dst) {
+  uint32_t o[16];
+  nib8_to_e4m3(p0.x, o[0], o[1]);
+  nib8_to_e4m3(p0.y, o[2], o[3]);
+  nib8_to_e4m3(p0.z, o[4], o[5]);
+  nib8_to_e4m3(p0.w, o[6], o[7]);
+  nib8_to_e4m3(p1.x, o[8], o[9]);
+  nib8_to_e4m3(p1.y, o[10], o[11]);
+  nib8_to_e4m3(p1.z, o[12], o[13]);
+  nib8_to_e4m3(p1.w, o[14], o[15]);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  d[2] = make_uint4(o[8], o[9], o[10], o[11]);
+  d[3] = make_uint4(o[12], o[13], o[14], o[15]);
+}
+
+// The scale of one row / column, split into bf16 pieces and laid out as the
+// two k-slot halves of a 32x32x16 bf16 MFMA operand.  Slot pairs (A x B):
+// (h,h) (h,m) (h,l) (m,h) (m,m) (m,l) (l,h) (l,m) in half 0, (l,l) in half 1.
+__device__ __forceinline__ void scale_pieces(float s, bool a_side, uint4& half0, uint4& half1) {
+  uint32_t h, m, l;
+  split3(s, h, m, l);
+  const uint4 a = make_uint4(h | (h << 16), h | (m << 16), m | (m << 16), l | (l << 16));
+  const uint4 b = make_uint4(h | (m << 16), l | (h << 16), m | (l << 16), h | (m << 16));
+  half0 = make_uint4(a_side ? a.x : b.x, a_side ? a.y : b.y, a_side ? a.z : b.z,
+                     a_side ? a.w : b.w);
+  half1 = make_uint4(l, 0, 0, 0);
+}
+
 template <int RK, bool YBF16, bool BBF16>
 __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint16_t* __restrict__ LR, int M, int K, int N,
     const uint8_t* __restrict__ W, const float* __restrict__ sW,
     const uint16_t* __restrict__ up, const void* __restrict__ bias, void* __restrict__ Y) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = int64_t(blockIdx.y) * BM, n0 = int64_t(blockIdx.x) * BN;
+  // separate LDS objects, so that the compiler can tell the DMA targets apart
+  // from the buffers the MFMAs read (no waits on an in-flight DMA)
+  __shared__ Stage st0, st1;
+  __shared__ Packed pkb0, pkb1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wm = wave >> 2, wn = wave & 3;
+  const int h = lane >> 5, r32 = lane & 31;
+  const uint32_t hm = h ? 0u : 0xFFFFFFFFu;   // k-slot half 1 carries one piece pair
+
+  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
+  // give each XCD a contiguous run of tiles (M fastest) to share its L2.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
   const int G = K / 64;
   const int64_t KP = K / 2;
 
-  v16f acc[2][2];
+  // staging role: waves 0..3 stage the 256 A rows of the tile (64 each),
+  // waves 4..7 the 256 B rows; thread tid widens row tid % 256 of its side.
+  // Rows past the matrix edge fetch the last row instead: their products only
+  // reach accumulator rows / columns that are never stored, so the main loop
+  // needs neither branches nor masks.
+  const bool is_a = wave < BM / 64;
+  const int srow = tid & (BM - 1);
+  const int rows_total = is_a ? M : N;
+  const int64_t row0 = is_a ? m0 : n0;
+  const int soff = (is_a ? 0 : int(offsetof(Stage, b))) + srow * LDS_ROW;
+  const int sidx = (is_a ? int(offsetof(Stage, sa)) : int(offsetof(Stage, sb))) + srow * 16;
+  const uint8_t* const gbase = is_a ? A : W;
+  const float* const sbase = is_a ? sA : sW;
+  // per-lane byte offsets (within one group's slab) of the two code transfers
+  // and of the scale transfer
+  const int wrow = (wave & 3) * 64;
+  const int64_t rc0 = row0 + wrow + (lane >> 1), rs = row0 + wrow + lane;
+  const int last = rows_total - 1;
+  const uint32_t off0 = uint32_t(rc0 < rows_total ? rc0 : last) * 32u + (lane & 1) * 16u;
+  const uint32_t off1 = uint32_t(rc0 + 32 < rows_total ? rc0 + 32 : last) * 32u + (lane & 1) * 16u;
+  const uint32_t offs = uint32_t(rs < rows_total ? rs : last) * 4u;
+
+  // DMA of one group's packed codes and scales into LDS; no registers are
+  // held while it is in flight
+  auto dma = [&](int g, Packed& pk) {
+    const uint8_t* gg = gbase + int64_t(g) * rows_total * 32;
+    const uint8_t* gs = reinterpret_cast<const uint8_t*>(sbase + int64_t(g) * rows_total);
+    __builtin_amdgcn_global_load_lds(gg + off0, (lds_ptr_t)&pk.code[wave][0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gg + off1, (lds_ptr_t)&pk.code[wave][1024], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gs + offs, (lds_ptr_t)&pk.scale[wave * 64], 4, 0, 0);
+  };
+  // The staged row's 32 packed bytes.  Read in an asm block that waits for
+  // its own result: the compiler's wait-count tracking does not tell DMA
+  // targets apart and would otherwise wait for the DMA started this step.
+  auto fetch_words = [&](const Packed& pk, v4i& w0, v4i& w1) {
+    typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
+    const uint32_t addr = uint32_t(reinterpret_cast<uintptr_t>((lds_cptr)&pk.code[wave][lane * 32]));
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(w0), "=v"(w1) : "v"(addr));
+  };
+  auto fetch4 = [&](const Packed& pk, int half, v4i& w) {
+    typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
+    const uint32_t addr =
+        uint32_t(reinterpret_cast<uintptr_t>((lds_cptr)&pk.code[wave][lane * 32 + half * 16]));
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(w) : "v"(addr));
+  };
+  // widen packed word `word` (index w) into 8 E4M3 bytes at LDS offset 8w
+  // LDS stores of the widened codes / scale pieces go through asm as well:
+  // the compiler would wait for every DMA in flight before any LDS store.
+  typedef __attribute__((address_space(3))) uint8_t* lds_bptr;
+  auto lds_addr = [](void* p) { return uint32_t(reinterpret_cast<uintptr_t>((lds_bptr)p)); };
+  auto widen_all = [&](uint8_t* stage_base, const Packed& pk) {
+    v4i w0, w1;
+    fetch_words(pk, w0, w1);
+    const uint32_t a = lds_addr(stage_base + soff);
+    lds_store_b64<0>(a, widen8(uint32_t(w0[0])));
+    lds_store_b64<8>(a, widen8(uint32_t(w0[1])));
+    lds_store_b64<16>(a, widen8(uint32_t(w0[2])));
+    lds_store_b64<24>(a, widen8(uint32_t(w0[3])));
+    lds_store_b64<32>(a, widen8(uint32_t(w1[0])));
+    lds_store_b64<40>(a, widen8(uint32_t(w1[1])));
+    lds_store_b64<48>(a, widen8(uint32_t(w1[2])));
+    lds_store_b64<56>(a, widen8(uint32_t(w1[3])));
+  };
+  // the same, spread over the MFMA blocks: word pair p = 0..3
+  v4i pw;
+  auto widen_pair = [&](uint8_t* stage_base, int p) {
+    const uint32_t a = lds_addr(stage_base + soff);
+    switch (p) {
+      case 0:
+        lds_store_b64<0>(a, widen8(uint32_t(pw[0])));
+        lds_store_b64<8>(a, widen8(uint32_t(pw[1])));
+        break;
+      case 1:
+        lds_store_b64<16>(a, widen8(uint32_t(pw[2])));
+        lds_store_b64<24>(a, widen8(uint32_t(pw[3])));
+        break;
+      case 2:
+        lds_store_b64<32>(a, widen8(uint32_t(pw[0])));
+        lds_store_b64<40>(a, widen8(uint32_t(pw[1])));
+        break;
+      default:
+        lds_store_b64<48>(a, widen8(uint32_t(pw[2])));
+        lds_store_b64<56>(a, widen8(uint32_t(pw[3])));
+        break;
+    }
+  };
+  auto pieces = [&](uint8_t* stage_base, const Packed& pk) {
+    float sv;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(sv) : "v"(lds_addr((void*)&pk.scale[tid])));
+    uint4 p0, p1;
+    scale_pieces(sv, is_a, p0, p1);
+    const v4i q0 = {int(p0.x), int(p0.y), int(p0.z), int(p0.w)};
+    const v4i q1 = {int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
+    const uint32_t a = lds_addr(stage_base + sidx);
+    lds_store_b128<0>(a, q0);
+    lds_store_b128<BM * 16>(a, q1);
+  };
+
+  v16f acc[RBL][CBL];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RBL; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < CBL; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  const v16f zero = acc[0][0];
+  v16f zero;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) zero[e] = 0.f;
 
-  // staging assignment: thread t loads 16 packed bytes (32 nibbles) of
-  // row t/2, half t%2, for A and for B
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const bool aok = m0 + lrow < M, bok = n0 + lrow < N;
-  const uint8_t* ap = A + (m0 + lrow) * KP + lhalf * 16;
-  const uint8_t* bp = W + (n0 + lrow) * KP + lhalf * 16;
+  uint8_t* const stage0 = reinterpret_cast<uint8_t*>(&st0);
+  uint8_t* const stage1 = reinterpret_cast<uint8_t*>(&st1);
 
-  for (int g = 0; g < G; ++g) {
-    uint4 pa = make_uint4(0, 0, 0, 0), pb = pa;
-    if (aok) pa = *reinterpret_cast<const uint4*>(ap + g * 32);
-    if (bok) pb = *reinterpret_cast<const uint4*>(bp + g * 32);
-    float sav = 0.f, sbv = 0.f;
-    if (tid < BM) {
-      if (m0 + tid < M) sav = sA[(m0 + tid) * G + g];
-    } else {
-      if (n0 + tid - BM < N) sbv = sW[(n0 + tid - BM) * G + g];
+  // Integer products of two blocks in flight (block b uses P[b & 1]), the
+  // scale outer product of one.
+  v16f P[2], S;
+  v8i fb[CBL], fa;
+  v4i qa;
+  auto load_b = [&](const Stage& cs) {
+#pragma unroll
+    for (int j = 0; j < CBL; ++j) {
+      const int rb = wn * WN + j * 32 + r32;
+      fb[j] = lds_frag(cs.b + rb * LDS_ROW + h * 32);
     }
-    __syncthreads();   // previous group's LDS reads are done
+  };
+  auto load_qb = [&](const Stage& cs, int j) {
+    const uint4 w = cs.sb[h][wn * WN + j * 32 + r32];
+    return v4i{int(w.x), int(w.y), int(w.z), int(w.w)};
+  };
+  auto load_fa = [&](const Stage& cs, int i) {
+    fa = lds_frag(cs.a + (wm * WM + i * 32 + r32) * LDS_ROW + h * 32);
+  };
+  auto load_qa = [&](const Stage& cs, int i) {
+    const uint4 w = cs.sa[h][wm * WM + i * 32 + r32];
+    qa = v4i{int(w.x), int(w.y), int(w.z), int(w.w)};
+  };
+  auto mfma_p = [&](int b) {          // block b = (i = b / 2, j = b % 2)
+    P[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[b & 1], zero, 0, 0, 0,
+                                                              127, 0, 127);
+  };
+  auto mfma_s = [&](int b, const v4i& qbj) {
+    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, qa),
+                                                __builtin_bit_cast(v8bf, qbj), zero, 0, 0, 0);
+    (void)b;
+  };
+  auto fma_block = [&](int b) {
+    const int i = b >> 1, j = b & 1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(S[e], P[b & 1][e], acc[i][j][e]);
+  };
+
+  // One K-group.  Per block b: the integer-product MFMA of block b+1 is
+  // issued, then the FMAs of block b, then the scale MFMA of block b+1, so
+  // the matrix core always has queued work while the vector ALU applies the
+  // scales.  The FMAs of block 7 run after the barrier, while the next
+  // group's fragments load.  The next group's codes (in registers) are
+  // widened into `nxt` in between; on the last group this fills the idle
+  // buffer with data nobody reads, which keeps the loop body branch-free.
+  auto group_step = [&](const uint8_t* cur, uint8_t* nxt, const Packed& pk_next, Packed& pk_free,
+                        bool tail, int gdma) {
+    const Stage& cs = *reinterpret_cast<const Stage*>(cur);
+    dma(gdma, pk_free);                 // two groups ahead, into the buffer freed last step
+    load_b(cs);
+    load_fa(cs, 0);
+    load_qa(cs, 0);
+    mfma_p(0);
     {
-      uint32_t o[8];
-      nib8_to_e4m3(pa.x, o[0], o[1]);
-      nib8_to_e4m3(pa.y, o[2], o[3]);
-      nib8_to_e4m3(pa.z, o[4], o[5]);
-      nib8_to_e4m3(pa.w, o[6], o[7]);
-      uint4* d = reinterpret_cast<uint4*>(sm.a + lrow * LDS_ROW + lhalf * 32);
-      d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      nib8_to_e4m3(pb.x, o[0], o[1]);
-      nib8_to_e4m3(pb.y, o[2], o[3]);
-      nib8_to_e4m3(pb.z, o[4], o[5]);
-      nib8_to_e4m3(pb.w, o[6], o[7]);
-      d = reinterpret_cast<uint4*>(sm.b + lrow * LDS_ROW + lhalf * 32);
-      d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      const v4i qb0 = load_qb(cs, 0);
+      if (tail) fma_block(7);             // previous group's last block
+      mfma_s(0, qb0);
     }
-    if (tid < BM) {
-      // A-side pieces for slot pairs (h,h) (h,m) (h,l) (m,h) (m,m) (m,l) (l,h) (l,m) | (l,l)
-      uint32_t h, m, l;
-      split3(sav, h, m, l);
-      sm.sa[tid][0] = h | (h << 16);
-      sm.sa[tid][1] = h | (m << 16);
-      sm.sa[tid][2] = m | (m << 16);
-      sm.sa[tid][3] = l | (l << 16);
-    } else {
-      uint32_t h, m, l;
-      split3(sbv, h, m, l);
-      sm.sb[tid - BM][0] = h | (m << 16);
-      sm.sb[tid - BM][1] = l | (h << 16);
-      sm.sb[tid - BM][2] = m | (l << 16);
-      sm.sb[tid - BM][3] = h | (m << 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 7; ++b) {
+      const bool new_row = (b & 1) == 1;      // block b+1 starts row block (b+1)/2
+      mfma_p(b + 1);
+      const v4i qbn = load_qb(cs, (b + 1) & 1);
+      if (!new_row && b + 2 < 8) load_fa(cs, (b + 2) >> 1);
+      fma_block(b);
+      mfma_s(b + 1, qbn);
+      if (!new_row && b + 2 < 8) load_qa(cs, (b + 2) >> 1);
+      if (b == 3) {
+        // no fragment load pending here: wait for the previous step's DMA
+        // and fetch the first packed words of group g+1
+        __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
+        fetch4(pk_next, 0, pw);
+      }
+      if (b == 5) fetch4(pk_next, 1, pw);
+      if (b >= 3) widen_pair(nxt, b - 3);
+      if (b == 6) pieces(nxt, pk_next);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    // fragments: lane l -> row (l % 32) of the block, bytes 32*(l/32) .. +32
-    v8i fa[2], fb[2];
-    v4i qa[2], qb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ra = wm * 64 + i * 32 + (lane & 31);
-      const int rb = wn * 64 + i * 32 + (lane & 31);
-      const uint4* pa4 = reinterpret_cast<const uint4*>(sm.a + ra * LDS_ROW + (lane >> 5) * 32);
-      const uint4* pb4 = reinterpret_cast<const uint4*>(sm.b + rb * LDS_ROW + (lane >> 5) * 32);
-      uint4 a0 = pa4[0], a1 = pa4[1], b0 = pb4[0], b1 = pb4[1];
-      fa[i] = v8i{int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
-      fb[i] = v8i{int(b0.x), int(b0.y), int(b0.z), int(b0.w), int(b1.x), int(b1.y), int(b1.z), int(b1.w)};
-      // S operands: k-slot half 0 carries 8 piece pairs, half 1 the ninth
-      if (lane < 32) {
-        qa[i] = v4i{int(sm.sa[ra][0]), int(sm.sa[ra][1]), int(sm.sa[ra][2]), int(sm.sa[ra][3])};
-        qb[i] = v4i{int(sm.sb[rb][0]), int(sm.sb[rb][1]), int(sm.sb[rb][2]), int(sm.sb[rb][3])};
-      } else {
-        qa[i] = v4i{int(sm.sa[ra][3] & 0xFFFFu), 0, 0, 0};
-        qb[i] = v4i{int(sm.sb[rb][2] >> 16), 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], zero, 0, 0, 0,
-                                                                127, 0, 127);
-        v16f s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, qa[i]),
-                                                         __builtin_bit_cast(v8bf, qb[j]),
-                                                         zero, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(s[e], p[e], acc[i][j][e]);
-      }
+  // prologue: groups 0 and 1 by DMA, group 0 widened into stage 0
+  dma(0, pkb0);
+  dma(G > 1 ? 1 : 0, pkb1);
+  __builtin_amdgcn_s_waitcnt(0x0F73);    // group 0 landed
+  widen_all(stage0, pkb0);
+  pieces(stage0, pkb0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+
+  // step for group g reads stage g%2, widens group g+1 (packed buffer
+  // (g+1)%2) into the other stage and DMAs group g+2 into packed buffer g%2;
+  // groups in pairs so that buffers are static
+  group_step(stage0, stage1, pkb1, pkb0, false, G > 2 ? 2 : G - 1);
+  int g = 1;
+  for (; g + 1 < G; g += 2) {
+    group_step(stage1, stage0, pkb0, pkb1, true, g + 2 < G ? g + 2 : G - 1);
+    group_step(stage0, stage1, pkb1, pkb0, true, g + 3 < G ? g + 3 : G - 1);
   }
+  if (g < G) group_step(stage1, stage0, pkb0, pkb1, true, G - 1);
+  fma_block(7);
 
   // ------------------------------------------------ epilogue: LR . up^T
   if constexpr (RK > 0) {
     const int R = RK * 16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t ra = m0 + wm * 64 + i * 32 + (lane & 31);
+    for (int kk = 0; kk < RK; ++kk) {
+      const int kof = kk * 16 + h * 8;
+      v4i ub[CBL];
 #pragma unroll
-      for (int kk = 0; kk < RK; ++kk) {
-        const int kof = kk * 16 + (lane >> 5) * 8;
+      for (int j = 0; j < CBL; ++j) {
+        const int64_t nb = n0 + wn * WN + j * 32 + r32;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (nb < N) u = *reinterpret_cast<const uint4*>(up + nb * R + kof);
+        ub[j] = v4i{int(u.x), int(u.y), int(u.z), int(u.w)};
+      }
+#pragma unroll
+      for (int i = 0; i < RBL; ++i) {
+        const int64_t ra = m0 + wm * WM + i * 32 + r32;
         uint4 la = make_uint4(0, 0, 0, 0);
         if (ra < M) la = *reinterpret_cast<const uint4*>(LR + ra * R + kof);
-        v4i lai = {int(la.x), int(la.y), int(la.z), int(la.w)};
+        const v4i lai = {int(la.x), int(la.y), int(la.z), int(la.w)};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t nb = n0 + wn * 64 + j * 32 + (lane & 31);
-          uint4 ub = make_uint4(0, 0, 0, 0);
-          if (nb < N) ub = *reinterpret_cast<const uint4*>(up + nb * R + kof);
-          v4i ubi = {int(ub.x), int(ub.y), int(ub.z), int(ub.w)};
+        for (int j = 0; j < CBL; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(v8bf, lai), __builtin_bit_cast(v8bf, ubi), acc[i][j], 0, 0, 0);
-        }
+              __builtin_bit_cast(v8bf, lai), __builtin_bit_cast(v8bf, ub[j]), acc[i][j], 0, 0, 0);
       }
     }
   }
@@ -224,15 +439,15 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   // ------------------------------------------------ bias, convert, store
   // 32x32 f32 MFMA result: lane l holds column l%32, rows 8(e/4) + 4(l/32) + e%4
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < CBL; ++j) {
+    const int64_t n = n0 + wn * WN + j * 32 + r32;
     if (n >= N) continue;
     const float bv = bias ? (BBF16 ? load_bias<uint16_t>(bias, n) : load_bias<float>(bias, n)) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RBL; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int64_t m = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
         if (m < M) {
           const float v = acc[i][j][e] + bv;
           if (YBF16)
@@ -244,11 +459,12 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   }
 }
 
+
 template <int RK>
 svdq_status launch_rk(const uint8_t* A, const float* sA, const uint16_t* LR, int M, int K,
                       int N, const uint8_t* W, const float* sW, const uint16_t* up,
                       const void* bias, bool bbf16, void* Y, bool ybf16, hipStream_t s) {
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  dim3 grid(unsigned(((M + BM - 1) / BM) * ((N + BN - 1) / BN)));
   if (ybf16) {
     if (bbf16)
       hipLaunchKernelGGL((gemm_int4_kernel<RK, true, true>), grid, dim3(NT), 0, s, A, sA, LR,

@@ -218,8 +218,9 @@ __global__ __launch_bounds__(256) void residual_int4_kernel(
     nib = q < 0 ? uint32_t(8 | -q) : uint32_t(q);
   }
   const uint32_t nb = __shfl_down(nib, 1);
-  if ((lane & 1) == 0) wcodes[n * (K / 2) + k / 2] = uint8_t(nib | (nb << 4));
-  if (lane == 0) wscales[n * G + g] = s;
+  // group-major: wcodes[K/64][N][32 bytes], wscales[K/64][N]
+  if ((lane & 1) == 0) wcodes[(int64_t(g) * N + n) * 32 + lane / 2] = uint8_t(nib | (nb << 4));
+  if (lane == 0) wscales[int64_t(g) * N + n] = s;
   if (residual) residual[n * K + k] = R;
 }
 
