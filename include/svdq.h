@@ -49,8 +49,10 @@
  *  are contiguous.
  *  INT4 group scales: float32, group-major [K/64][rows], scale =
  *  fl32(absmax / 7).
- *  NVFP4 codes: E2M1 nibbles (bit 3 = sign), same packing; block scales are
- *  E4M3 bytes [rows, K/16]; one float32 tensor scale per tensor.
+ *  NVFP4 codes: E2M1 nibbles (bit 3 = sign), same packing and the same
+ *  chunk-major layout [K/64][rows][32 bytes]; block scales are E4M3 bytes,
+ *  [K/64][rows][4] (the four blocks of 16 of each 64-wide chunk); one float32
+ *  tensor scale per tensor.
  *  AWQ codes: unsigned nibbles 0..15, same packing; scales and zero points
  *  bf16 [N, K/group].
  */
@@ -88,7 +90,7 @@ const char* svdq_last_error(void);
  * 256; 0 for invalid arguments).  Layout from the start of the workspace,
  * each part 256-byte aligned:
  *   INT4 : A codes [K/64][M][32] bytes, sA f32 [K/64][M], LR bf16 [M, rank]
- *   NVFP4: A codes u8 [M, K/2], sA E4M3 u8 [M, K/16], LR bf16 [M, rank]  */
+ *   NVFP4: A codes [K/64][M][32] bytes, sA E4M3 u8 [K/64][M][4], LR bf16 [M, rank] */
 size_t svdq_workspace_bytes(int64_t M, int64_t K, int32_t rank, svdq_precision prec);
 
 /* Byte offsets of the three workspace parts (same layout as above). */
@@ -111,7 +113,7 @@ svdq_status svdq_act_absmax(const void* X, svdq_dtype x_dtype, int64_t M, int64_
  *   R[n,k]   = fl32(Wh[n,k] - lam_k * sum_i lora_up[n,i] lora_down[i,k])
  *   INT4 : wcodes, wscales (f32 [K/64][N]) = Q4(R)
  *   NVFP4: ts_w = fl32(max|R| / 2688) (1 if 0); wcodes, wscales (E4M3 u8
- *          [N, K/16]) = blockwise FP4 of R; ts_x = fl32(max_k fl32(act_amax[k]
+ *          [K/64][N][4]) = blockwise FP4 of R; ts_x = fl32(max_k fl32(act_amax[k]
  *          smooth_k) / 2688) (1 if 0), the static activation tensor scale.
  *
  * The SVD is computed by block subspace iteration (oversampling 16) with a
@@ -124,8 +126,8 @@ svdq_status svdq_act_absmax(const void* X, svdq_dtype x_dtype, int64_t M, int64_
  * rank: 0 <= rank <= min(N, K).  K % 64 == 0.
  * Outputs (DEVICE): smooth f32 [K]; lora_down bf16 [rank, K]; lora_up bf16
  * [N, rank] (inputs instead when flags has SVDQ_LOWRANK_GIVEN); wcodes u8
- * N*K/2 bytes (INT4: group-major [K/64][N][32]; NVFP4: [N, K/2]); wscales
- * (INT4: f32 [K/64][N]; NVFP4: E4M3 u8 [N, K/16]); w_tensor_scale, x_tensor_scale f32 [1]
+ * N*K/2 bytes, chunk-major [K/64][N][32]; wscales (INT4: f32 [K/64][N];
+ * NVFP4: E4M3 u8 [K/64][N][4]); w_tensor_scale, x_tensor_scale f32 [1]
  * (NVFP4 only; may be NULL for INT4); residual f32 [N, K] or NULL.
  * Temporary device memory is allocated and freed inside the call. */
 svdq_status svdq_quantize_weights(const float* W, int64_t N, int64_t K,
@@ -145,11 +147,11 @@ svdq_status svdq_quantize_weights(const float* W, int64_t N, int64_t K,
  *   LR[m, i] = bf16(sum_k bf16(X[m,k]) lora_down[i,k])  (fp32 accumulation)
  * X: DEVICE [M, K] x_dtype.  smooth f32 [K]; lora_down bf16 [rank, K];
  * x_tensor_scale DEVICE f32 [1] (NVFP4; ignored for INT4).
- * Outputs DEVICE: codes M*K/2 bytes (INT4: group-major [K/64][M][32]; NVFP4:
- * [M, K/2]); scales (INT4: f32 [K/64][M]; NVFP4: E4M3 u8 [M, K/16]); LR bf16
- * [M, rank] (rank 0: LR may be NULL).
- * M >= 0 (0 launches nothing), K % 64 == 0 (INT4) / K % 16 == 0 (NVFP4),
- * rank % 16 == 0, 0 <= rank <= 256. */
+ * Outputs DEVICE: codes M*K/2 bytes, chunk-major [K/64][M][32]; scales
+ * (INT4: f32 [K/64][M]; NVFP4: E4M3 u8 [K/64][M][4]); LR bf16 [M, rank]
+ * (rank 0: LR may be NULL).
+ * M >= 0 (0 launches nothing), K % 64 == 0, rank % 16 == 0,
+ * 0 <= rank <= 256. */
 svdq_status svdq_act_quantize(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
                               int32_t rank, svdq_precision prec, const float* smooth,
                               const uint16_t* lora_down, const float* x_tensor_scale,

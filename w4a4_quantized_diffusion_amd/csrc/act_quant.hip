@@ -9,8 +9,8 @@
 //   per block: E4M3 block scale, E2M1 codes      (NVFP4, blocks of 16)
 //   LR = bf16(X) . lora_down^T                   (low-rank down-projection)
 //
-// Output layout (INT4): group-major, codes[K/64][M][32 bytes] and
-// scales[K/64][M]; NVFP4 keeps row-major codes[M][K/2], scales[M][K/16].
+// Output layout: chunk-major along K, codes[K/64][M][32 bytes]; scales
+// [K/64][M] (INT4, f32) or [K/64][M][4] (NVFP4, E4M3 bytes).
 //
 // Work split: a workgroup of 4 waves owns 16 rows; wave w takes the K-groups
 // w, w+4, ... so that at every step the 4 waves read adjacent 128-byte
@@ -193,7 +193,6 @@ __global__ __launch_bounds__(256) void act_quant_nvfp4_kernel(
   const int64_t row = row0 + r;
   const bool ok = row < M;
   const int G = K / 64;            // 64-wide steps: 4 NVFP4 blocks each
-  const int KB = K / 16;
   const float ts = *ts_x;
   const float d = 6.0f * ts;
   v4f acc[RB > 0 ? RB : 1];
@@ -235,13 +234,15 @@ __global__ __launch_bounds__(256) void act_quant_nvfp4_kernel(
       }
     }
     if (ok) {
-      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + row * (K / 2));
-      cp[k0 / 8] = w[0];
-      cp[k1 / 8] = w[1];
+      // chunk-major: codes[K/64][M][32 bytes], scales[K/64][M][4]
+      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + (int64_t(g) * M + row) * 32);
+      cp[q] = w[0];
+      cp[4 + q] = w[1];
       // lanes with even quarter hold the first half of each block
       if ((q & 1) == 0) {
-        scales[row * KB + k0 / 16] = uint8_t(sb[0]);
-        scales[row * KB + k1 / 16] = uint8_t(sb[1]);
+        uint8_t* sp = scales + (int64_t(g) * M + row) * 4;
+        sp[q >> 1] = uint8_t(sb[0]);
+        sp[2 + (q >> 1)] = uint8_t(sb[1]);
       }
     }
     lr_mfma<RB>(acc, b0, down, K, r, k0);

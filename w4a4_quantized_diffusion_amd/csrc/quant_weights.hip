@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void act_tensor_scale_kernel(const float* __re
 // NVFP4 pass 2: one lane per element, 16-lane blocks.
 __global__ __launch_bounds__(256) void nvfp4_block_quant_kernel(const float* __restrict__ R,
                                                                 const float* __restrict__ ts_p,
-                                                                int64_t total, int K,
+                                                                int64_t total, int N, int K,
                                                                 uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ sbout) {
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -281,10 +281,13 @@ __global__ __launch_bounds__(256) void nvfp4_block_quant_kernel(const float* __r
   const uint32_t e = den > 0.f ? e2m1_rne_sat(z / den) : 0u;
   const uint32_t eb = __shfl_down(e, 1);
   if (ok) {
-    if ((idx & 1) == 0) codes[idx / 2] = uint8_t(e | (eb << 4));
-    if ((idx & 15) == 0) sbout[idx / 16] = uint8_t(sb);
+    // chunk-major: codes[K/64][N][32 bytes], scales[K/64][N][4]
+    const int64_t n = idx / K;
+    const int k = int(idx % K);
+    const int64_t chunk = int64_t(k >> 6) * N + n;
+    if ((idx & 1) == 0) codes[chunk * 32 + ((k & 63) >> 1)] = uint8_t(e | (eb << 4));
+    if ((idx & 15) == 0) sbout[chunk * 4 + ((k & 63) >> 4)] = uint8_t(sb);
   }
-  (void)K;
 }
 
 // AWQ: one wave per (row, group of 64).
@@ -571,7 +574,7 @@ svdq_status quantize_weights_impl(const float* W, int64_t N64, int64_t K64,
                        lam.as<float>(), down, up, N, K, rank, R, ramax.as<float>());
     hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(1), 0, s, ramax.as<float>(), ts_w);
     hipLaunchKernelGGL(nvfp4_block_quant_kernel, dim3(blocks(total, 256)), dim3(256), 0, s, R,
-                       ts_w, total, K, wcodes, static_cast<uint8_t*>(wscales));
+                       ts_w, total, N, K, wcodes, static_cast<uint8_t*>(wscales));
     hipLaunchKernelGGL(act_tensor_scale_kernel, dim3(1), dim3(256), 0, s, act_amax, smooth, K,
                        ts_x);
     st = check_launch("residual_nvfp4");

@@ -136,12 +136,13 @@ def svdq_quantize_weights(W, act_amax, rank, prec="int4", lowrank=None, residual
     else:
         out["lora_down"] = _empty((rank, K), torch.int16, dev)
         out["lora_up"] = _empty((N, rank), torch.int16, dev)
-    if pr == INT4:       # group-major [K/64][N][32] codes, [K/64][N] scales
-        out["wcodes"] = _empty((K // 64, N, 32), torch.uint8, dev)
+    # chunk-major along K: codes [K/64][N][32]; scales [K/64][N] f32 (INT4)
+    # or [K/64][N][4] E4M3 bytes (NVFP4)
+    out["wcodes"] = _empty((K // 64, N, 32), torch.uint8, dev)
+    if pr == INT4:
         out["wscales"] = _empty((K // 64, N), torch.float32, dev)
     else:
-        out["wcodes"] = _empty((N, K // 2), torch.uint8, dev)
-        out["wscales"] = _empty((N, K // 16), torch.uint8, dev)
+        out["wscales"] = _empty((K // 64, N, 4), torch.uint8, dev)
     out["w_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev)
     out["x_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev)
     out["residual"] = _empty((N, K), torch.float32, dev) if residual else None
@@ -154,16 +155,16 @@ def svdq_quantize_weights(W, act_amax, rank, prec="int4", lowrank=None, residual
 
 
 def svdq_act_quantize(X, layer, codes=None, scales=None, LR=None):
-    """The activation kernel alone: returns (codes, scales, LR).  INT4 codes
-    are group-major [K/64][M][32], scales [K/64][M]."""
+    """The activation kernel alone: returns (codes, scales, LR).  Codes are
+    chunk-major [K/64][M][32]; scales [K/64][M] f32 (INT4) or [K/64][M][4]
+    E4M3 bytes (NVFP4)."""
     M, K = X.shape
     rank, pr, dev = layer["rank"], layer["prec"], X.device
     if codes is None:
-        codes = (_empty((K // 64, M, 32), torch.uint8, dev) if pr == INT4
-                 else _empty((M, K // 2), torch.uint8, dev))
+        codes = _empty((K // 64, M, 32), torch.uint8, dev)
     if scales is None:
         scales = (_empty((K // 64, M), torch.float32, dev) if pr == INT4
-                  else _empty((M, K // 16), torch.uint8, dev))
+                  else _empty((K // 64, M, 4), torch.uint8, dev))
     if LR is None and rank:
         LR = _empty((M, rank), torch.int16, dev)
     _check(lib().svdq_act_quantize(
@@ -175,7 +176,7 @@ def svdq_act_quantize(X, layer, codes=None, scales=None, LR=None):
 
 def svdq_gemm_w4a4(codes, scales, LR, layer, bias=None, y_dtype=torch.float32, Y=None):
     """The GEMM with its epilogue alone, on the activation kernel's outputs."""
-    M = codes.shape[1] if layer["prec"] == INT4 else codes.shape[0]
+    M = codes.shape[1]
     K, N, rank, pr = layer["K"], layer["N"], layer["rank"], layer["prec"]
     if Y is None:
         Y = _empty((M, N), y_dtype, codes.device)
@@ -209,12 +210,11 @@ def workspace_views(workspace, M, K, rank, prec="int4"):
     """(codes, scales, LR) views of a workspace filled by svdq_linear_w4a4."""
     pr = _PREC[prec]
     c, s, l = svdq_workspace_layout(M, K, rank, pr)
+    codes = workspace[c:c + M * (K // 2)].view(K // 64, M, 32)
     if pr == INT4:
-        codes = workspace[c:c + M * (K // 2)].view(K // 64, M, 32)
         scales = workspace[s:s + M * (K // 64) * 4].view(torch.float32).view(K // 64, M)
     else:
-        codes = workspace[c:c + M * (K // 2)].view(M, K // 2)
-        scales = workspace[s:s + M * (K // 16)].view(M, K // 16)
+        scales = workspace[s:s + M * (K // 16)].view(K // 64, M, 4)
     lr = workspace[l:l + M * rank * 2].view(torch.int16).view(M, rank) if rank else None
     return codes, scales, lr
 
