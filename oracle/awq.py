@@ -14,8 +14,14 @@ For each output row n and group of 64 weights w:
   s == 0: z = 0, q = 0
   else:   z = clamp(rne(fl32(-mn / s)), 0, 15)
           q = clamp(rne(fl32(w / s)) + z, 0, 15)
-Codes are unsigned nibbles, two per byte, even k in the low nibble.
-Y = X @ ((q - z) * s)^T + b.
+Codes are unsigned nibbles, two per byte, even k in the low nibble.  A zero
+point is an integer; zero is stored as +0.
+
+W4A16 means 4-bit storage and a 16-bit multiply.  The pages leave the
+precision of the dequantized weight open; the reading used here is the
+activations' type: wd = bf16((q - z) s), rounded once from the exact product
+(4-bit integer times 8-bit significand).  Then
+Y = X @ wd^T + b, summed exactly (float64).
 """
 
 import numpy as np
@@ -40,6 +46,7 @@ def quantize_weights(w, group=GROUP):
     sd = s[:, :, None]
     safe = np.where(sd > 0, sd, 1.0)
     z = np.where(s > 0, np.clip(rne_int(fl32(-mn / np.where(s > 0, s, 1.0))), 0, 15), 0.0)
+    z = z + 0.0                              # an integer: -0 becomes +0
     q = np.where(sd > 0,
                  np.clip(rne_int(fl32(wg / safe)) + z[:, :, None], 0, 15), 0.0)
     q = q.reshape(n, k).astype(np.uint8)
@@ -52,10 +59,15 @@ def dequantize(q, s, z, group=GROUP):
     return ((qg - z[:, :, None]) * s[:, :, None]).reshape(n, k)
 
 
+def dequantize_bf16(q, s, z, group=GROUP):
+    """The 16-bit weights the multiply uses: bf16((q - z) s)."""
+    return bf16(dequantize(q, s, z, group))
+
+
 def linear_w4a16(x, q, s, z, bias=None, group=GROUP):
-    """Y = X @ dequant(q, s, z)^T + b in float64.  x: [M, K] float32 values
+    """Y = X @ bf16((q - z) s)^T + b in float64.  x: [M, K] float32 values
     (bf16 inputs passed as their values)."""
-    wd = dequantize(q, s, z, group)
+    wd = dequantize_bf16(q, s, z, group)
     y = np.asarray(x, dtype=F64) @ wd.T
     if bias is not None:
         y += np.asarray(bias, dtype=F64)[None, :]

@@ -98,9 +98,41 @@ def test_awq_on_grid_is_lossless():
     w = ((q0.reshape(n, 2, 64) - z0[:, :, None]) * s0[:, :, None]).reshape(n, k).astype(np.float32)
     q, s, z, packed = awq.quantize_weights(w)
     assert np.array_equal(s, s0) and np.array_equal(z, z0) and np.array_equal(q, q0)
+    # power-of-two scales: (q - z) s has at most 4 significant bits, so the
+    # 16-bit weights are the weights themselves and Y is the exact product
+    s2 = np.ldexp(1.0, g.integers(-10, -4, (n, k // 64)))
+    w2 = ((q0.reshape(n, 2, 64) - z0[:, :, None]) * s2[:, :, None]).reshape(n, k).astype(np.float32)
+    q2, s2q, z2, _ = awq.quantize_weights(w2)
     x = g.standard_normal((4, k)).astype(np.float32)
+    y = awq.linear_w4a16(x, q2, s2q, z2)
+    assert np.allclose(y, x.astype(np.float64) @ w2.astype(np.float64).T, rtol=0, atol=1e-12)
+
+
+def test_awq_bf16_weight_rounding_bound():
+    """The 16-bit weights differ from the exact dequantized ones by at most
+    half a bf16 step (2^-8 relative: 8 significant bits), so
+    |Y - X wd_exact^T| <= 2^-8 sum|x||wd|;
+    and they are bf16 values."""
+    g = np.random.default_rng(34)
+    w = (g.standard_normal((24, 192)) * 0.05).astype(np.float32)
+    q, s, z, _ = awq.quantize_weights(w)
+    wd = awq.dequantize(q, s, z)
+    wb = awq.dequantize_bf16(q, s, z)
+    assert np.array_equal(F.bf16(wb), wb)
+    assert np.all(np.abs(wb - wd) <= 2.0 ** -8 * np.abs(wd))
+    assert np.any(wb != wd)                  # 12-bit products do get rounded
+    x = g.standard_normal((5, 192)).astype(np.float32)
     y = awq.linear_w4a16(x, q, s, z)
-    assert np.allclose(y, x.astype(np.float64) @ w.astype(np.float64).T, rtol=0, atol=1e-12)
+    exact = x.astype(np.float64) @ wd.T
+    assert np.all(np.abs(y - exact) <= 2.0 ** -8 * (np.abs(x) @ np.abs(wd).T) + 1e-12)
+
+
+def test_awq_zero_points_are_positive_zero():
+    w = np.zeros((1, 128), np.float32)
+    w[0, :64] = np.linspace(0.0, 1.0, 64)        # min 0: zero point 0
+    _, s, z, _ = awq.quantize_weights(w)
+    assert z[0, 0] == 0 and not np.signbit(z[0, 0])
+    assert z[0, 1] == 0 and not np.signbit(z[0, 1]) and s[0, 1] == 0
 
 
 def test_awq_error_bound():
