@@ -53,8 +53,8 @@
  *  chunk-major layout [K/64][rows][32 bytes]; block scales are E4M3 bytes,
  *  [K/64][rows][4] (the four blocks of 16 of each 64-wide chunk); one float32
  *  tensor scale per tensor.
- *  AWQ codes: unsigned nibbles 0..15, same packing; scales and zero points
- *  bf16 [N, K/group].
+ *  AWQ codes: unsigned nibbles 0..15, same packing and chunk-major layout
+ *  [K/64][N][32 bytes]; scales and zero points bf16 [K/64][N].
  */
 #ifndef SVDQ_H
 #define SVDQ_H
@@ -193,15 +193,18 @@ svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64
  *   mn = min(min w, 0), mx = max(max w, 0), s = bf16(fl32(fl32(mx - mn) / 15))
  *   s == 0: z = 0, q = 0;  else z = clamp(rne(fl32(-mn / s)), 0, 15),
  *   q = clamp(rne(fl32(w / s)) + z, 0, 15).
- * W DEVICE f32 [N, K]; outputs DEVICE q u8 [N, K/2] (unsigned nibbles),
- * scales, zeros bf16 [N, K/group].  group == 64, K % 64 == 0. */
+ * W DEVICE f32 [N, K]; outputs DEVICE q u8 [K/64][N][32] (unsigned nibbles),
+ * scales, zeros bf16 [K/64][N].  group == 64, K % 64 == 0. */
 svdq_status awq_quantize_weights(const float* W, int64_t N, int64_t K, int32_t group,
                                  uint8_t* q, uint16_t* scales, uint16_t* zeros,
                                  hipStream_t stream);
 
-/* AWQ W4A16 linear: Y = X . ((q - z) s)^T + bias, fp32 accumulation with
- * the group scale applied to the exact per-group sums.
- * X DEVICE bf16 [M, K]; bias bf16 [N] or NULL; Y [M, N] y_dtype.
+/* AWQ W4A16 linear: Y = X . wd^T + bias with wd = bf16((q - z) s) (the
+ * product is exact in fp32 and rounded once to bf16), bf16 MFMAs with fp32
+ * accumulation.  M <= 64 runs a weight-streaming kernel, larger M a tiled
+ * one; both give the same kind of result (order of the fp32 sums differs).
+ * X DEVICE bf16 [M, K]; q / scales / zeros as written by awq_quantize_weights;
+ * bias bf16 [N] or NULL; Y [M, N] y_dtype.
  * M >= 0, N % 16 == 0, group == 64, K % 64 == 0. */
 svdq_status awq_linear_w4a16(const uint16_t* X, int64_t M, int64_t K, int64_t N,
                              int32_t group, const uint8_t* q, const uint16_t* scales,

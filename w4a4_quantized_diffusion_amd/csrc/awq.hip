@@ -1,8 +1,347 @@
+// AWQ W4A16 linear layer (weight-only INT4), gfx950.
+//
+//   Y[m,n] = sum_k X[m,k] wd[n,k] + b[n],   wd = bf16((q - z) s)
+//
+// The chaosnode.de page ("Nunchaku Lite vs. Original", "Hardware-Support")
+// lists awq_w4a16 INT4 as the second quantized layer type next to
+// svdq_w4a4; the aiphreaks.com page ("Technical Breakdown") notes that
+// weight-only schemes save memory but not compute.  q are unsigned nibbles
+// (even k in the low nibble), s and z bf16 per row and group of 64 along K,
+// all chunk-major: q [K/64][N][32 bytes], s and z [K/64][N].
+//
+// Dequantization: (q - z) s is computed exactly in fp32 (as fma(q, s, -z s):
+// the products of a 4-bit integer and an 8-bit bf16 significand are exact)
+// and rounded once to bf16; the bf16 MFMAs accumulate in fp32.
+//
+// Two kernels:
+//  * M <= 64 (decode-style calls): the layer is bound by reading the 4-bit
+//    weights.  A workgroup owns 32 output columns; its 4 waves split K and
+//    dequantize straight into the B operand of v_mfma_f32_16x16x32_bf16 in
+//    registers (no LDS staging), one 16-row tile of X at a time, then reduce
+//    their partial sums through LDS in a fixed order.
+//  * larger M: 256 x 256 workgroup tiles, 4 waves of 128 x 128 on
+//    v_mfma_f32_32x32x16_bf16.  Per 64-wide K chunk each thread copies one X
+//    row (bf16, 128 bytes) and dequantizes one weight row into the LDS buffer
+//    the MFMAs are not reading, one chunk ahead; one barrier per chunk.
+
 #include "internal.h"
-namespace svdq {
-svdq_status launch_awq_linear(const uint16_t*, int64_t, int64_t, int64_t, const uint8_t*,
-                              const uint16_t*, const uint16_t*, const uint16_t*, void*,
-                              svdq_dtype, hipStream_t) {
-  return fail(SVDQ_ERR_UNSUPPORTED, "AWQ linear not built yet");
+
+#include <type_traits>
+
+using namespace svdq_dev;
+
+namespace {
+
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
 }
+
+// 8 unsigned nibbles (one dword, even k low) -> 8 bf16 values (q - z) s in
+// k order, as 4 dwords.  zs = -z s (exact in fp32).
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float zs) {
+  const uint32_t e = w & 0x0F0F0F0Fu, o = (w >> 4) & 0x0F0F0F0Fu;
+  // (byte i) -> float: the compiler selects v_cvt_f32_ubyte<i>
+  const float q0 = float(e & 0xFFu), q1 = float(o & 0xFFu);
+  const float q2 = float((e >> 8) & 0xFFu), q3 = float((o >> 8) & 0xFFu);
+  const float q4 = float((e >> 16) & 0xFFu), q5 = float((o >> 16) & 0xFFu);
+  const float q6 = float(e >> 24), q7 = float(o >> 24);
+  return make_uint4(pk_bf16(fmaf(q0, s, zs), fmaf(q1, s, zs)),
+                    pk_bf16(fmaf(q2, s, zs), fmaf(q3, s, zs)),
+                    pk_bf16(fmaf(q4, s, zs), fmaf(q5, s, zs)),
+                    pk_bf16(fmaf(q6, s, zs), fmaf(q7, s, zs)));
+}
+
+__device__ __forceinline__ void store_y(void* Y, bool ybf16, int64_t idx, float v) {
+  if (ybf16)
+    static_cast<uint16_t*>(Y)[idx] = f32_to_bf16(v);
+  else
+    static_cast<float*>(Y)[idx] = v;
+}
+
+// ------------------------------------------------------------ M <= 64
+
+constexpr int SK_NT = 256;     // 4 waves
+constexpr int SK_COLS = 32;    // output columns per workgroup (2 tiles of 16)
+
+template <int MT>
+__global__ __launch_bounds__(SK_NT) void awq_skinny_kernel(
+    const uint16_t* __restrict__ X, int M, int K, int N, const uint8_t* __restrict__ q,
+    const uint16_t* __restrict__ sc, const uint16_t* __restrict__ zr,
+    const uint16_t* __restrict__ bias, void* __restrict__ Y, bool ybf16) {
+  __shared__ float red[4][MT][2][4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane >> 4, r = lane & 15;
+  const int64_t n0 = int64_t(blockIdx.x) * SK_COLS;
+  const int G = K / 64;
+
+  v4f acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[mt][t] = v4f{0, 0, 0, 0};
+
+  // B operand slot (j, i) of the MFMA for K half h is k = 16 j + 8 h + i, so
+  // lane (j, r) of tile t dequantizes bytes 8j .. 8j+7 of row n0 + 16t + r:
+  // one 8-byte load per tile and chunk.  The A operand uses the same k map.
+  for (int c = wave; c < G; c += 4) {
+    uint2 wq[2];
+    float s[2], zs[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t n = n0 + 16 * t + r;
+      const int64_t nc = n < N ? n : N - 1;
+      wq[t] = *reinterpret_cast<const uint2*>(q + (int64_t(c) * N + nc) * 32 + 8 * j);
+      s[t] = bf16_to_f32(sc[int64_t(c) * N + nc]);
+      zs[t] = -bf16_to_f32(zr[int64_t(c) * N + nc]) * s[t];
+    }
+    uint4 b[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      b[t][0] = dequant8(wq[t].x, s[t], zs[t]);
+      b[t][1] = dequant8(wq[t].y, s[t], zs[t]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + r;
+      uint4 a[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+      if (m < M) {
+        const uint4* xp = reinterpret_cast<const uint4*>(X + int64_t(m) * K + 64 * c + 16 * j);
+        a[0] = xp[0];
+        a[1] = xp[1];
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf, a[hh]), __builtin_bit_cast(v8bf, b[t][hh]), acc[mt][t],
+              0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][mt][t][e][lane] = acc[mt][t][e];
+  __syncthreads();
+  if (wave != 0) return;
+  // 16x16 f32 MFMA result: lane l holds column l%16, rows 4(l/16) + e
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int64_t n = n0 + 16 * t + r;
+    if (n >= N) continue;
+    const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mt + 4 * j + e;
+        if (m >= M) continue;
+        const float v = ((red[0][mt][t][e][lane] + red[1][mt][t][e][lane]) +
+                         (red[2][mt][t][e][lane] + red[3][mt][t][e][lane])) + bv;
+        store_y(Y, ybf16, int64_t(m) * N + n, v);
+      }
+  }
+}
+
+// ------------------------------------------------------------ large M
+
+constexpr int BM = 256, BN = 256;
+constexpr int NT = 256;
+constexpr int WM = 128, WN = 128;
+constexpr int RBL = WM / 32, CBL = WN / 32;
+constexpr int ROWB = 144;               // 64 bf16 values (128 bytes) + 16 pad
+constexpr int STAGE = (BM + BN) * ROWB;
+
+struct Chunk {
+  uint4 x0, x1, x2, x3, x4, x5, x6, x7;   // 64 bf16 of the A row
+  uint4 w0, w1;                           // 64 nibbles of the B row
+  float s, zs;
+};
+
+// 16-byte piece I of the staged A row (I a compile-time constant)
+template <int I>
+__device__ __forceinline__ uint4 xpiece(const Chunk& c) {
+  if constexpr (I == 0) return c.x0;
+  else if constexpr (I == 1) return c.x1;
+  else if constexpr (I == 2) return c.x2;
+  else if constexpr (I == 3) return c.x3;
+  else if constexpr (I == 4) return c.x4;
+  else if constexpr (I == 5) return c.x5;
+  else if constexpr (I == 6) return c.x6;
+  else return c.x7;
+}
+
+__global__ __launch_bounds__(NT) void awq_gemm_kernel(
+    const uint16_t* __restrict__ X, int M, int K, int N, const uint8_t* __restrict__ q,
+    const uint16_t* __restrict__ sc, const uint16_t* __restrict__ zr,
+    const uint16_t* __restrict__ bias, void* __restrict__ Y, bool ybf16) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+
+  // XCD-aware tile order, M fastest (workgroups are dealt round-robin to the
+  // 8 XCDs; a contiguous run per XCD shares the weight columns in its L2)
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
+  const int G = K / 64;
+
+  // thread tid stages A row tid and B row tid; rows past the edge repeat the
+  // last row (their products only reach outputs that are never stored)
+  const int64_t ra = m0 + tid < M ? m0 + tid : M - 1;
+  const int64_t rb = n0 + tid < N ? n0 + tid : N - 1;
+  auto load_chunk = [&](int g, Chunk& ch) {
+    const uint4* xp = reinterpret_cast<const uint4*>(X + ra * K + 64 * g);
+    ch.x0 = xp[0];
+    ch.x1 = xp[1];
+    ch.x2 = xp[2];
+    ch.x3 = xp[3];
+    ch.x4 = xp[4];
+    ch.x5 = xp[5];
+    ch.x6 = xp[6];
+    ch.x7 = xp[7];
+    const uint4* wp = reinterpret_cast<const uint4*>(q + (int64_t(g) * N + rb) * 32);
+    ch.w0 = wp[0];
+    ch.w1 = wp[1];
+    ch.s = bf16_to_f32(sc[int64_t(g) * N + rb]);
+    ch.zs = -bf16_to_f32(zr[int64_t(g) * N + rb]) * ch.s;
+  };
+  // quarter P (k 16P .. 16P+15) of a staged chunk into LDS; P is a
+  // compile-time constant so the chunk stays in registers
+  auto stage_quarter = [&](uint8_t* st, const Chunk& ch, auto PC) {
+    constexpr int P = decltype(PC)::value;
+    uint4* da = reinterpret_cast<uint4*>(st + tid * ROWB + P * 32);
+    da[0] = xpiece<2 * P>(ch);
+    da[1] = xpiece<2 * P + 1>(ch);
+    const uint32_t w0 = P == 0 ? ch.w0.x : P == 1 ? ch.w0.z : P == 2 ? ch.w1.x : ch.w1.z;
+    const uint32_t w1 = P == 0 ? ch.w0.y : P == 1 ? ch.w0.w : P == 2 ? ch.w1.y : ch.w1.w;
+    uint4* db = reinterpret_cast<uint4*>(st + (BM + tid) * ROWB + P * 32);
+    db[0] = dequant8(w0, ch.s, ch.zs);
+    db[1] = dequant8(w1, ch.s, ch.zs);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  v16f acc[RBL][CBL];
+#pragma unroll
+  for (int i = 0; i < RBL; ++i)
+#pragma unroll
+    for (int jj = 0; jj < CBL; ++jj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
+
+  Chunk ch0, ch1;
+  load_chunk(0, ch0);
+  if (G > 1) load_chunk(1, ch1);
+  stage_quarter(lds, ch0, I0{});
+  stage_quarter(lds, ch0, I1{});
+  stage_quarter(lds, ch0, I2{});
+  stage_quarter(lds, ch0, I3{});
+  __syncthreads();
+
+  const int aoff = (wm * WM + r32) * ROWB + h * 16;
+  const int boff = (BM + wn * WN + r32) * ROWB + h * 16;
+
+  auto step = [&](int g, const uint8_t* st, uint8_t* nx, const Chunk& nch,
+                  Chunk& fch) __attribute__((always_inline)) {
+    v4i fa[2][RBL], fb[2][CBL];
+    auto frags = [&](int ks, v4i (&a)[RBL], v4i (&b)[CBL]) {
+#pragma unroll
+      for (int i = 0; i < RBL; ++i)
+        a[i] = *reinterpret_cast<const v4i*>(st + aoff + i * 32 * ROWB + ks * 32);
+#pragma unroll
+      for (int jj = 0; jj < CBL; ++jj)
+        b[jj] = *reinterpret_cast<const v4i*>(st + boff + jj * 32 * ROWB + ks * 32);
+    };
+    frags(0, fa[0], fb[0]);
+    const bool more = g + 1 < G;
+    auto sub = [&](auto KC) {
+      constexpr int ks = decltype(KC)::value;
+      if (ks < 3) frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < RBL; ++i)
+#pragma unroll
+        for (int jj = 0; jj < CBL; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(v8bf, fa[ks & 1][i]), __builtin_bit_cast(v8bf, fb[ks & 1][jj]),
+              acc[i][jj], 0, 0, 0);
+      if (more) stage_quarter(nx, nch, KC);
+    };
+    sub(I0{});
+    sub(I1{});
+    sub(I2{});
+    sub(I3{});
+    if (g + 2 < G) load_chunk(g + 2, fch);
+    __syncthreads();
+  };
+
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    step(g, lds, lds + STAGE, ch1, ch0);
+    step(g + 1, lds + STAGE, lds, ch0, ch1);
+  }
+  if (g < G) step(g, lds, lds + STAGE, ch1, ch0);
+
+  // 32x32 f32 MFMA result: lane l holds column l%32, rows 8(e/4) + 4(l/32) + e%4
+#pragma unroll
+  for (int jj = 0; jj < CBL; ++jj) {
+    const int64_t n = n0 + wn * WN + jj * 32 + r32;
+    if (n >= N) continue;
+    const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < RBL; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) store_y(Y, ybf16, m * N + n, acc[i][jj][e] + bv);
+      }
+  }
+}
+
+}  // namespace
+
+namespace svdq {
+
+svdq_status launch_awq_linear(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                              const uint8_t* q, const uint16_t* scales, const uint16_t* zeros,
+                              const uint16_t* bias, void* Y, svdq_dtype y_dt, hipStream_t s) {
+  if (M == 0) return SVDQ_OK;
+  const bool yb = y_dt == SVDQ_BF16;
+  if (M <= 64) {
+    dim3 grid(unsigned((N + SK_COLS - 1) / SK_COLS));
+    const int mt = int((M + 15) / 16);
+#define SVDQ_SK(T)                                                                          \
+  hipLaunchKernelGGL(awq_skinny_kernel<T>, grid, dim3(SK_NT), 0, s, X, int(M), int(K), int(N), \
+                     q, scales, zeros, bias, Y, yb)
+    switch (mt) {
+      case 1: SVDQ_SK(1); break;
+      case 2: SVDQ_SK(2); break;
+      case 3: SVDQ_SK(3); break;
+      default: SVDQ_SK(4); break;
+    }
+#undef SVDQ_SK
+    return check_launch("awq_skinny");
+  }
+  const size_t shm = 2 * size_t(STAGE);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(awq_gemm_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
+    return fail(SVDQ_ERR_HIP, "awq_gemm: shared memory size");
+  dim3 grid(unsigned(((M + BM - 1) / BM) * ((N + BN - 1) / BN)));
+  hipLaunchKernelGGL(awq_gemm_kernel, grid, dim3(NT), shm, s, X, int(M), int(K), int(N), q,
+                     scales, zeros, bias, Y, yb);
+  return check_launch("awq_gemm");
+}
+
 }  // namespace svdq

@@ -166,7 +166,8 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
   // stage `nx` a block at a time in between, then the chunk after next
   // fetched into fa_ / fb_ (whose contents were decoded the previous step).
   auto step = [&](int g, const uint8_t* st, uint8_t* nx, const PackedRow& na,
-                  const PackedRow& nb, PackedRow& fa_, PackedRow& fb_) {
+                  const PackedRow& nb, PackedRow& fa_, PackedRow& fb_)
+                  __attribute__((always_inline)) {
     v4i fa[2][RBL], fb[2][CBL];
     auto frags = [&](int ks, v4i (&a)[RBL], v4i (&b)[CBL]) {
 #pragma unroll

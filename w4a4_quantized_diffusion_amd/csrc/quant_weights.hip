@@ -310,14 +310,15 @@ __global__ __launch_bounds__(256) void awq_quant_kernel(const float* __restrict_
   float z = 0.f;
   uint32_t code = 0;
   if (s != 0.f) {
-    z = fminf(fmaxf(rintf(-mn / s), 0.f), 15.f);
+    z = fminf(fmaxf(rintf(-mn / s), 0.f), 15.f) + 0.f;   // an integer: never -0
     code = uint32_t(fminf(fmaxf(rintf(w / s) + z, 0.f), 15.f));
   }
   const uint32_t cb = __shfl_down(code, 1);
-  if ((lane & 1) == 0) q[n * (K / 2) + k / 2] = uint8_t(code | (cb << 4));
+  // chunk-major: q[K/64][N][32 bytes], scales / zeros [K/64][N]
+  if ((lane & 1) == 0) q[(int64_t(g) * N + n) * 32 + lane / 2] = uint8_t(code | (cb << 4));
   if (lane == 0) {
-    scales[n * G + g] = sbits;
-    zeros[n * G + g] = f32_to_bf16(z);
+    scales[int64_t(g) * N + n] = sbits;
+    zeros[int64_t(g) * N + n] = f32_to_bf16(z);
   }
 }
 

@@ -222,9 +222,10 @@ def workspace_views(workspace, M, K, rank, prec="int4"):
 def awq_quantize_weights(W, group=64):
     N, K = W.shape
     dev = W.device
-    q = _empty((N, K // 2), torch.uint8, dev)
-    s = _empty((N, K // group), torch.int16, dev)
-    z = _empty((N, K // group), torch.int16, dev)
+    # chunk-major along K: q [K/64][N][32], scales / zeros [K/64][N]
+    q = _empty((K // group, N, 32), torch.uint8, dev)
+    s = _empty((K // group, N), torch.int16, dev)
+    z = _empty((K // group, N), torch.int16, dev)
     _check(lib().awq_quantize_weights(_p(W), N, K, group, _p(q), _p(s), _p(z), _stream()))
     return dict(q=q, scales=s, zeros=z, N=N, K=K, group=group)
 
