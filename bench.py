@@ -10,9 +10,11 @@ library's own svdq_quantize_weights.
 
 Prints one JSON line: TOPS = 2 M N K / (time per step), the roofline of the
 dominant kernel (the GEMM) measured with HIP events on the launch stream, and
-the CPU oracle's throughput on a bounded sample of the same workload.
+the CPU oracle's throughput on a bounded sample of the same workload.  The
+same line carries, under "other_paths", the NVFP4 precision at the MLP
+up-projection shape and the AWQ W4A16 layer at M = 1, 16, 4608.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-other-paths]
 """
 
 import argparse
@@ -25,6 +27,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_FP8_TOPS = 5000.0          # MI355X dense FP8 / INT8 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0        # dense fp16 / bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP4_TFLOPS = 10100.0       # dense fp4 / fp6 MFMA
 
 
 def parse():
@@ -35,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--nbuf", type=int, default=4, help="distinct X / Y buffers rotated")
+    ap.add_argument("--no-other-paths", action="store_true",
+                    help="skip the NVFP4 and AWQ W4A16 measurements")
+    ap.add_argument("--other-steps", type=int, default=20)
     return ap.parse_args()
 
 
@@ -94,6 +102,97 @@ def cpu_baseline(M, K, N, R, seconds):
     return {"value": tops, "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": f"{rows} of {M} rows of the same layer (full K={K}, N={N}, rank {R}), "
                       f"{t:.1f} s, numpy/BLAS on the host"}
+
+
+def time_calls(fn, steps, warmup=3):
+    """Per-call durations (seconds) of fn(i), HIP events on the current
+    stream around each call."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+
+
+def other_paths(steps):
+    """The NVFP4 precision at the MLP up-projection shape (M 4608, K 3072 ->
+    N 12288, rank 32) and the AWQ W4A16 layer (K 3072 -> N 12288) at M = 1,
+    16 and 4608: seeded synthetic tensors, weights quantized by the library,
+    per-kernel HIP-event times.  Weight-streaming cases rotate enough weight
+    copies (> 512 MB) that the 256 MB last-level cache cannot hold them."""
+    import torch
+    from w4a4_quantized_diffusion_amd import svdq, synth
+    dev = torch.device("cuda:0")
+    res = {}
+
+    # NVFP4, MLP up-projection
+    M, K, N, R = 4608, 3072, 12288, 32
+    s = synth.layer(M, K, N, R, seed=0, workload="mlp_fp4")
+    x = torch.from_numpy(s["x"]).to(dev).to(torch.bfloat16)
+    bias = torch.from_numpy(s["b"]).to(dev).to(torch.bfloat16)
+    amax = svdq.svdq_act_absmax(x)
+    lay = svdq.svdq_quantize_weights(torch.from_numpy(s["w"]).to(dev), amax, R, "nvfp4")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(svdq.svdq_workspace_bytes(M, K, R, "nvfp4"), dtype=torch.uint8, device=dev)
+    codes, scales, lr = svdq.workspace_views(ws, M, K, R, "nvfp4")
+    t_lin = time_calls(lambda i: svdq.svdq_linear_w4a4(x, lay, bias, workspace=ws, Y=y), steps)
+    t_act = time_calls(lambda i: svdq.svdq_act_quantize(x, lay, codes, scales, lr), steps)
+    t_gem = time_calls(lambda i: svdq.svdq_gemm_w4a4(codes, scales, lr, lay, bias, Y=y), steps)
+    ops = 2.0 * M * N * K
+    act_bytes = M * K * 2 + M * K // 2 + M * K // 16 + M * R * 2 + K * 4 + R * K * 2
+    res["nvfp4_mlp_up"] = {
+        "workload": "NVFP4 (E2M1 b16, E4M3 block scales), rank 32, M 4608 x K 3072 -> N 12288",
+        "linear_us": round(float(t_lin.mean()) * 1e6, 2),
+        "TOPS": round(ops / t_lin.mean() / 1e12, 1),
+        "gemm_nvfp4": {"avg_us": round(float(t_gem.mean()) * 1e6, 2),
+                       "TFLOP/s": round(ops / t_gem.mean() / 1e12, 1), "bound": "mfma (f16)",
+                       "frac_f16_peak": round(ops / t_gem.mean() / 1e12 / PEAK_F16_TFLOPS, 4),
+                       "frac_fp4_peak": round(ops / t_gem.mean() / 1e12 / PEAK_FP4_TFLOPS, 4)},
+        "act_quant_nvfp4": {"avg_us": round(float(t_act.mean()) * 1e6, 2),
+                            "algorithmic_bytes": act_bytes,
+                            "GB/s": round(act_bytes / t_act.mean() / 1e9, 1),
+                            "frac_hbm": round(act_bytes / t_act.mean() / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    del x, lay, y, ws, codes, scales, lr
+    torch.cuda.empty_cache()
+
+    # AWQ W4A16
+    K, N = 3072, 12288
+    aw = synth.WORKLOADS["awq"]
+    w = torch.from_numpy(synth.gaussian((N, K), 0.02, 0, aw, 1)).to(dev)
+    base = svdq.awq_quantize_weights(w)
+    del w
+    wbytes = N * K // 2 + 2 * N * (K // 64) * 2
+    copies = max(1, int(512e6 // wbytes) + 1)
+    lays = [base] + [dict(base, q=base["q"].clone(), scales=base["scales"].clone(),
+                          zeros=base["zeros"].clone()) for _ in range(copies - 1)]
+    awq = {}
+    for m in (1, 16, 4608):
+        x = torch.from_numpy(synth.activations(m, K, 0, aw, 0)).to(dev).to(torch.bfloat16)
+        y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        nrot = copies if m <= 64 else 1
+        t = time_calls(lambda i: svdq.awq_linear_w4a16(x, lays[i % nrot], Y=y), steps)
+        byts = wbytes + m * K * 2 + m * N * 2
+        flops = 2.0 * m * N * K
+        r = {"avg_us": round(float(t.mean()) * 1e6, 2), "algorithmic_bytes": byts,
+             "GB/s": round(byts / t.mean() / 1e9, 1),
+             "frac_hbm": round(byts / t.mean() / 1e9 / PEAK_HBM_GBS, 4),
+             "TFLOP/s": round(flops / t.mean() / 1e12, 2),
+             "frac_bf16_peak": round(flops / t.mean() / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "bound": "hbm" if m <= 64 else "mfma (bf16)",
+             "weight_copies_rotated": nrot}
+        awq[f"M{m}"] = r
+    res["awq_w4a16"] = dict(workload="AWQ W4A16 INT4 g64, bf16 scales / zeros, K 3072 -> N 12288",
+                            **awq)
+    return res
 
 
 def main():
@@ -204,6 +303,10 @@ def main():
         },
         "gpu": torch.cuda.get_device_name(0),
     }
+    del xs, ys, ws, layer
+    torch.cuda.empty_cache()
+    if not args.no_other_paths:
+        out["other_paths"] = other_paths(args.other_steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(M, K, N, R, args.cpu_seconds)
     print(json.dumps(out), flush=True)
