@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-other-paths", action="store_true",
                     help="skip the NVFP4 and AWQ W4A16 measurements")
     ap.add_argument("--other-steps", type=int, default=20)
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first run a plain device copy of this many MiB three times "
+                         "(a known-size kernel to calibrate rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -209,6 +212,13 @@ def main():
     M, K, N, R = 4096, 3072, 12288, 32
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_mb:
+        src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     s = synth.layer(M, K, N, R, seed=0, workload="flagship")
     W = torch.from_numpy(s["w"]).to(dev)
     xs = [torch.from_numpy(s["x"]).to(dev).to(torch.bfloat16)]
