@@ -307,12 +307,14 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   // scale outer product of one.
   v16f P[2], S;
   v8i fb[CBL], fa;
-  v4i qa;
+  v4i qa, qb[CBL];
   auto load_b = [&](const Stage& cs) {
 #pragma unroll
     for (int j = 0; j < CBL; ++j) {
       const int rb = wn * WN + j * 32 + r32;
       fb[j] = lds_frag(cs.b + rb * LDS_ROW + h * 32);
+      const uint4 w = cs.sb[h][rb];
+      qb[j] = v4i{int(w.x), int(w.y), int(w.z), int(w.w)};
     }
   };
   auto load_qb = [&](const Stage& cs, int j) {
@@ -356,20 +358,23 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     load_fa(cs, 0);
     load_qa(cs, 0);
     mfma_p(0);
-    {
-      const v4i qb0 = load_qb(cs, 0);
-      if (tail) fma_block(7);             // previous group's last block
-      mfma_s(0, qb0);
-    }
+    if (tail) fma_block(7);             // previous group's last block
+    mfma_s(0, qb[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 7; ++b) {
       const bool new_row = (b & 1) == 1;      // block b+1 starts row block (b+1)/2
+      // issue order is fixed with scheduling barriers: the integer MFMA of
+      // block b+1 goes out before the FMAs of block b read the products of
+      // block b, so the two product buffers are live together (distinct
+      // registers) and the FMAs overlap the MFMA instead of waiting for it
       mfma_p(b + 1);
-      const v4i qbn = load_qb(cs, (b + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
       if (!new_row && b + 2 < 8) load_fa(cs, (b + 2) >> 1);
+      __builtin_amdgcn_sched_barrier(0);
       fma_block(b);
-      mfma_s(b + 1, qbn);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_s(b + 1, qb[(b + 1) & 1]);
       if (!new_row && b + 2 < 8) load_qa(cs, (b + 2) >> 1);
       if (b == 3) {
         // no fragment load pending here: wait for the previous step's DMA
@@ -437,25 +442,65 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   }
 
   // ------------------------------------------------ bias, convert, store
-  // 32x32 f32 MFMA result: lane l holds column l%32, rows 8(e/4) + 4(l/32) + e%4
+  // The 32x32 f32 MFMA result has lane l on column l%32, rows
+  // 8(e/4) + 4(l/32) + e%4: a direct store writes 2- or 4-byte pieces.  Each
+  // wave instead passes one 32-row block row at a time through a private LDS
+  // buffer (the stages are free now) and stores whole 16-byte row pieces.
+  __syncthreads();
+  constexpr int ER = WN + 4;                 // floats per LDS row (padded)
+  constexpr int EBYTES = 32 * ER * 4;        // one block row of one wave
+  static_assert(6 * EBYTES <= int(sizeof(Stage)) && 2 * EBYTES <= int(sizeof(Stage)),
+                "epilogue buffers must fit in the stages");
+  float* const eb = reinterpret_cast<float*>(
+      wave < 6 ? reinterpret_cast<uint8_t*>(&st0) + wave * EBYTES
+               : reinterpret_cast<uint8_t*>(&st1) + (wave - 6) * EBYTES);
+  float bv[CBL];
 #pragma unroll
   for (int j = 0; j < CBL; ++j) {
     const int64_t n = n0 + wn * WN + j * 32 + r32;
-    if (n >= N) continue;
-    const float bv = bias ? (BBF16 ? load_bias<uint16_t>(bias, n) : load_bias<float>(bias, n)) : 0.f;
+    bv[j] = (bias && n < N) ? (BBF16 ? load_bias<uint16_t>(bias, n) : load_bias<float>(bias, n))
+                            : 0.f;
+  }
+  const int64_t col0 = n0 + wn * WN;
 #pragma unroll
-    for (int i = 0; i < RBL; ++i)
+  for (int i = 0; i < RBL; ++i) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < M) {
-          const float v = acc[i][j][e] + bv;
-          if (YBF16)
-            static_cast<uint16_t*>(Y)[m * N + n] = f32_to_bf16(v);
-          else
-            static_cast<float*>(Y)[m * N + n] = v;
-        }
+    for (int j = 0; j < CBL; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        eb[(8 * (e >> 2) + 4 * h + (e & 3)) * ER + j * 32 + r32] = acc[i][j][e] + bv[j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t row0 = m0 + wm * WM + i * 32;
+    if (YBF16) {
+      // lane: rows lane/8 + 8t, columns 8 (lane%8) .. +8
+      const int q = lane & 7;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int rr = (lane >> 3) + 8 * t;
+        const float4 a = *reinterpret_cast<const float4*>(eb + rr * ER + 8 * q);
+        const float4 b = *reinterpret_cast<const float4*>(eb + rr * ER + 8 * q + 4);
+        const int64_t m = row0 + rr, n = col0 + 8 * q;
+        if (m < M && n < N)
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + m * N + n) =
+              make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                         pack_bf16x2(b.z, b.w));
       }
+    } else {
+      // lane: rows lane/16 + 4t, columns 4 (lane%16) .. +4
+      const int q = lane & 15;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rr = (lane >> 4) + 4 * t;
+        const float4 a = *reinterpret_cast<const float4*>(eb + rr * ER + 4 * q);
+        const int64_t m = row0 + rr, n = col0 + 4 * q;
+        if (m < M && n < N) *reinterpret_cast<float4*>(static_cast<float*>(Y) + m * N + n) = a;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
