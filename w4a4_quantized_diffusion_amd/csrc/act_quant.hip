@@ -12,10 +12,11 @@
 // Output layout: chunk-major along K, codes[K/64][M][32 bytes]; scales
 // [K/64][M] (INT4, f32) or [K/64][M][4] (NVFP4, E4M3 bytes).
 //
-// Work split: a workgroup of 4 waves owns 16 rows; wave w takes the K-groups
-// w, w+4, ... so that at every step the 4 waves read adjacent 128-byte
-// pieces of each row.  Lane l owns row (l % 16) and the two 8-element
-// chunks k = 64g + 8(l/16) + [0, 8) and +32: exactly the A-operand slice of
+// Work split: a workgroup of 8 waves owns 16 rows; wave w takes the K-groups
+// w, w+8, ... so that at every step the 8 waves read adjacent 128-byte
+// pieces of each row, and keeps the X loads of its next 4 groups in flight
+// (the kernel is bound by reading X).  Lane l owns row (l % 16) and the two
+// 8-element chunks k = 64g + 8(l/16) + [0, 8) and +32: exactly the A-operand slice of
 // a 16x16x32 bf16 MFMA, so the down-projection needs no data movement.
 // The per-wave LR partial sums are reduced in a fixed order through LDS
 // (deterministic).
@@ -32,46 +33,117 @@ using namespace svdq_dev;
 namespace {
 
 constexpr int ROWS = 16;      // rows per workgroup
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;
+constexpr int DEPTH = 3;      // K-groups of X in flight per wave
 
-__device__ __forceinline__ void load8(const void* X, bool f32, int64_t off, bool ok,
-                                      float (&x)[8], uint32_t (&xb)[4]) {
-  if (f32) {
-    float4 a = make_float4(0, 0, 0, 0), b = a;
-    if (ok) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(X) + off);
-      a = p[0];
-      b = p[1];
-    }
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+// The raw X bytes of one lane for one 64-wide K group: elements k0 .. k0+7
+// and k0+32 .. k0+39 (f32: four 16-byte pieces, bf16: two).
+template <bool XF32>
+struct XRaw {
+  uint4 v[XF32 ? 4 : 2];
+};
+
+// lora_down fragments of one lane for one K group (both 8-wide chunks, all
+// 16-row blocks of the rank), prefetched with X when the rank is small
+constexpr int RB_PREFETCH = 2;
+template <int RB>
+struct DownRaw {
+  uint4 v[RB > 0 && RB <= RB_PREFETCH ? 2 * RB : 1];
+};
+
+template <int RB>
+__device__ __forceinline__ void load_down(const uint16_t* __restrict__ down, int K, int r, int k0,
+                                          DownRaw<RB>& d) {
+  if constexpr (RB > 0 && RB <= RB_PREFETCH) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
-  } else {
-    uint4 a = make_uint4(0, 0, 0, 0);
-    if (ok) a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(X) + off);
-    xb[0] = a.x; xb[1] = a.y; xb[2] = a.z; xb[3] = a.w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = __uint_as_float(xb[j] << 16);
-      x[2 * j + 1] = __uint_as_float(xb[j] & 0xFFFF0000u);
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint16_t* p = down + int64_t(rb * 16 + r) * K + k0;
+      d.v[2 * rb] = *reinterpret_cast<const uint4*>(p);
+      d.v[2 * rb + 1] = *reinterpret_cast<const uint4*>(p + 32);
     }
   }
 }
 
-__device__ __forceinline__ void load_smooth8(const float* smooth, int k, float (&s)[8]) {
-  const float4* p = reinterpret_cast<const float4*>(smooth + k);
-  float4 a = p[0], b = p[1];
-  s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
-  s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+// Rows past M load row M-1 (no branch, so the loads stay in flight in
+// order); the caller zeroes those lanes' values.
+template <bool XF32>
+__device__ __forceinline__ void load_raw(const void* X, int64_t off0, XRaw<XF32>& r) {
+  if constexpr (XF32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(X) + off0);
+    r.v[0] = p[0];
+    r.v[1] = p[1];
+    r.v[2] = p[8];
+    r.v[3] = p[9];
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(X) + off0);
+    r.v[0] = p[0];
+    r.v[1] = p[4];
+  }
 }
 
-// rne(fl32(z / s)) for |z| <= 7 s, exact (see the file comment).
-__device__ __forceinline__ float quot_rne(float z, float s, float inv, bool fast) {
-  float t = z * inv;
-  float fr = fabsf(t - truncf(t));
-  if (!fast || fabsf(fr - 0.5f) <= 0x1p-19f) t = z / s;
-  return rintf(t);
+// raw bytes -> the 2 x 8 values as floats and as bf16 bit pairs
+template <bool XF32>
+__device__ __forceinline__ void unpack_raw(const XRaw<XF32>& r, bool ok, float (&x0)[8],
+                                           float (&x1)[8], uint32_t (&b0)[4],
+                                           uint32_t (&b1)[4]) {
+  const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
+  if constexpr (XF32) {
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(&r.v[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x0[j] = __uint_as_float(u[j] & keep);
+      x1[j] = __uint_as_float(u[8 + j] & keep);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b0[j] = pack_bf16x2(x0[2 * j], x0[2 * j + 1]);
+      b1[j] = pack_bf16x2(x1[2 * j], x1[2 * j + 1]);
+    }
+  } else {
+    const uint32_t w0[4] = {r.v[0].x & keep, r.v[0].y & keep, r.v[0].z & keep, r.v[0].w & keep};
+    const uint32_t w1[4] = {r.v[1].x & keep, r.v[1].y & keep, r.v[1].z & keep, r.v[1].w & keep};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b0[j] = w0[j];
+      b1[j] = w1[j];
+      x0[2 * j] = __uint_as_float(w0[j] << 16);
+      x0[2 * j + 1] = __uint_as_float(w0[j] & 0xFFFF0000u);
+      x1[2 * j] = __uint_as_float(w1[j] << 16);
+      x1[2 * j + 1] = __uint_as_float(w1[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+// The smooth factors of one lane's two 8-element chunks, fetched with the
+// X loads of the same group (a load issued later would be counted behind
+// every X load in flight and have to wait for all of them).
+struct SmoothRaw {
+  float4 v[4];
+};
+
+__device__ __forceinline__ void load_smooth(const float* __restrict__ smooth, int k0,
+                                            SmoothRaw& s) {
+  const float4* p = reinterpret_cast<const float4*>(smooth + k0);
+  s.v[0] = p[0];
+  s.v[1] = p[1];
+  s.v[2] = p[8];
+  s.v[3] = p[9];
+}
+
+__device__ __forceinline__ void unpack_smooth(const SmoothRaw& r, float (&s0)[8], float (&s1)[8]) {
+  const float* f = reinterpret_cast<const float*>(&r.v[0]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s0[j] = f[j];
+    s1[j] = f[8 + j];
+  }
+}
+
+// t = z fl32(1/s) lies within 2^-20 of fl32(z / s) for |z| <= 7 s; only a
+// t within 2^-19 of a half-integer can round differently from the quotient.
+__device__ __forceinline__ bool near_half(float t) {
+  const float fr = fabsf(t - truncf(t));
+  return fabsf(fr - 0.5f) <= 0x1p-19f;
 }
 
 // sign-magnitude nibble of an integer-valued float in [-7, 7]
@@ -91,6 +163,24 @@ __device__ __forceinline__ void lr_mfma(v4f (&acc)[RB > 0 ? RB : 1], const uint3
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       uint4 bu = *reinterpret_cast<const uint4*>(down + int64_t(rb * 16 + r) * K + k);
+      v4i bi = {int(bu.x), int(bu.y), int(bu.z), int(bu.w)};
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, bi),
+                                                         acc[rb], 0, 0, 0);
+    }
+  }
+}
+
+// lr_mfma with the lora_down fragments already in registers (half h: the
+// chunk at k0 or at k0 + 32)
+template <int RB>
+__device__ __forceinline__ void lr_mfma_pre(v4f (&acc)[RB > 0 ? RB : 1], const uint32_t (&xb)[4],
+                                            const DownRaw<RB>& d, int h) {
+  if constexpr (RB > 0 && RB <= RB_PREFETCH) {
+    v4i ai = {int(xb[0]), int(xb[1]), int(xb[2]), int(xb[3])};
+    v8bf a = __builtin_bit_cast(v8bf, ai);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint4 bu = d.v[2 * rb + h];
       v4i bi = {int(bu.x), int(bu.y), int(bu.z), int(bu.w)};
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, bi),
                                                          acc[rb], 0, 0, 0);
@@ -122,12 +212,13 @@ __device__ __forceinline__ void lr_reduce_store(v4f (&acc)[RB > 0 ? RB : 1], flo
 }
 
 template <int RB, bool XF32>
-__global__ __launch_bounds__(256) void act_quant_int4_kernel(
+__global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ down, uint8_t* __restrict__ codes,
     float* __restrict__ scales, uint16_t* __restrict__ LR) {
   extern __shared__ float red[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int64_t row0 = int64_t(blockIdx.x) * ROWS;
   const int64_t row = row0 + r;
@@ -137,14 +228,38 @@ __global__ __launch_bounds__(256) void act_quant_int4_kernel(
 #pragma unroll
   for (int i = 0; i < (RB > 0 ? RB : 1); ++i) acc[i] = v4f{0, 0, 0, 0};
 
-  for (int g = wave; g < G; g += WAVES) {
+  // wave w takes the K-groups w, w + WAVES, ...; the X loads of the next
+  // DEPTH groups are in flight while one is processed
+  const int T = (G - wave + WAVES - 1) / WAVES;
+  const int64_t xrow = ok ? row : M - 1;
+  XRaw<XF32> ring[DEPTH];
+  DownRaw<RB> dring[DEPTH];
+  SmoothRaw sring[DEPTH];
+  // every slot is always (re)loaded, past the last group with the last
+  // group's data, so that the ring keeps fixed registers and its loads stay
+  // in flight
+  auto fetch = [&](int tt, int sl_) __attribute__((always_inline)) {
+    const int gg = wave + WAVES * (tt < T ? tt : T - 1);
+    load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
+    load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
+    load_down<RB>(down, K, r, gg * 64 + 8 * q, dring[sl_]);
+  };
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
+  // straight-line slots: a slot past the last group runs on zeroed data and
+  // stores nothing (keeps the wait counts exact across the loop)
+  for (int t0 = 0; t0 < T; t0 += DEPTH)
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl) {
+    const int t = t0 + sl;
+    const bool live = t < T;
+    {
+    const int g = wave + WAVES * (live ? t : T - 1);
     const int k0 = g * 64 + 8 * q, k1 = k0 + 32;
     float x0[8], x1[8], s0[8], s1[8];
     uint32_t b0[4], b1[4];
-    load8(X, XF32, row * K + k0, ok, x0, b0);
-    load8(X, XF32, row * K + k1, ok, x1, b1);
-    load_smooth8(smooth, k0, s0);
-    load_smooth8(smooth, k1, s1);
+    unpack_raw<XF32>(ring[sl], ok && live, x0, x1, b0, b1);
+    unpack_smooth(sring[sl], s0, s1);
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -159,13 +274,31 @@ __global__ __launch_bounds__(256) void act_quant_int4_kernel(
     const bool fast = s >= 0x1p-126f;
     uint32_t w0 = 0, w1 = 0;
     if (s > 0.f) {
+      // quotients through the reciprocal; only when some lane of the wave
+      // has one within 2^-19 of a half-integer (or a tiny scale) does the
+      // wave take the exact divisions, for those values
+      float t0[8], t1[8];
+      bool need = !fast;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        w0 |= int4_nibble(quot_rne(x0[j], s, inv, fast)) << (4 * j);
-        w1 |= int4_nibble(quot_rne(x1[j], s, inv, fast)) << (4 * j);
+        t0[j] = x0[j] * inv;
+        t1[j] = x1[j] * inv;
+        need |= near_half(t0[j]) | near_half(t1[j]);
+      }
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (!fast || near_half(t0[j])) t0[j] = x0[j] / s;
+          if (!fast || near_half(t1[j])) t1[j] = x1[j] / s;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        w0 |= int4_nibble(rintf(t0[j])) << (4 * j);
+        w1 |= int4_nibble(rintf(t1[j])) << (4 * j);
       }
     }
-    if (ok) {
+    if (ok && live) {
       // group-major layout: the 32 bytes of (group g, row) follow those of
       // (g, row - 1), so the GEMM's loads of a group are contiguous
       uint32_t* cp = reinterpret_cast<uint32_t*>(codes + (int64_t(g) * M + row) * 32);
@@ -173,8 +306,16 @@ __global__ __launch_bounds__(256) void act_quant_int4_kernel(
       cp[4 + q] = w1;
       if (q == 0) scales[int64_t(g) * M + row] = s;
     }
-    lr_mfma<RB>(acc, b0, down, K, r, k0);
-    lr_mfma<RB>(acc, b1, down, K, r, k1);
+    if constexpr (RB <= RB_PREFETCH) {
+      lr_mfma_pre<RB>(acc, b0, dring[sl], 0);
+      lr_mfma_pre<RB>(acc, b1, dring[sl], 1);
+    } else {
+      lr_mfma<RB>(acc, b0, down, K, r, k0);
+      lr_mfma<RB>(acc, b1, down, K, r, k1);
+    }
+    // the slot is free: refill it with the group DEPTH steps ahead
+    fetch(t + DEPTH, sl);
+    }
   }
   lr_reduce_store<RB>(acc, red, row0, M, LR);
 }
@@ -182,12 +323,13 @@ __global__ __launch_bounds__(256) void act_quant_int4_kernel(
 // ---------------------------------------------------------------- NVFP4
 
 template <int RB, bool XF32>
-__global__ __launch_bounds__(256) void act_quant_nvfp4_kernel(
+__global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
     const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ down, const float* __restrict__ ts_x,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ LR) {
   extern __shared__ float red[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int64_t row0 = int64_t(blockIdx.x) * ROWS;
   const int64_t row = row0 + r;
@@ -199,14 +341,36 @@ __global__ __launch_bounds__(256) void act_quant_nvfp4_kernel(
 #pragma unroll
   for (int i = 0; i < (RB > 0 ? RB : 1); ++i) acc[i] = v4f{0, 0, 0, 0};
 
-  for (int g = wave; g < G; g += WAVES) {
+  const int T = (G - wave + WAVES - 1) / WAVES;
+  const int64_t xrow = ok ? row : M - 1;
+  XRaw<XF32> ring[DEPTH];
+  DownRaw<RB> dring[DEPTH];
+  SmoothRaw sring[DEPTH];
+  // every slot is always (re)loaded, past the last group with the last
+  // group's data, so that the ring keeps fixed registers and its loads stay
+  // in flight
+  auto fetch = [&](int tt, int sl_) __attribute__((always_inline)) {
+    const int gg = wave + WAVES * (tt < T ? tt : T - 1);
+    load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
+    load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
+    load_down<RB>(down, K, r, gg * 64 + 8 * q, dring[sl_]);
+  };
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
+  // straight-line slots: a slot past the last group runs on zeroed data and
+  // stores nothing (keeps the wait counts exact across the loop)
+  for (int t0 = 0; t0 < T; t0 += DEPTH)
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl) {
+    const int t = t0 + sl;
+    const bool live = t < T;
+    {
+    const int g = wave + WAVES * (live ? t : T - 1);
     const int k0 = g * 64 + 8 * q, k1 = k0 + 32;
     float x0[8], x1[8], s0[8], s1[8];
     uint32_t b0[4], b1[4];
-    load8(X, XF32, row * K + k0, ok, x0, b0);
-    load8(X, XF32, row * K + k1, ok, x1, b1);
-    load_smooth8(smooth, k0, s0);
-    load_smooth8(smooth, k1, s1);
+    unpack_raw<XF32>(ring[sl], ok && live, x0, x1, b0, b1);
+    unpack_smooth(sring[sl], s0, s1);
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -228,12 +392,24 @@ __global__ __launch_bounds__(256) void act_quant_nvfp4_kernel(
       if (den > 0.f) {
         const float inv = 1.0f / den;
         const bool fast = den >= 0x1p-126f && inv < 0x1p126f;
+        // as for INT4: the exact division only where the wave needs it
+        float tq[8];
+        bool need = !fast;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          w[h] |= e2m1_quot(h ? x1[j] : x0[j], den, inv, fast) << (4 * j);
+        for (int j = 0; j < 8; ++j) {
+          tq[j] = (h ? x1[j] : x0[j]) * inv;
+          need |= e2m1_near_mid(tq[j]);
+        }
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (!fast || e2m1_near_mid(tq[j])) tq[j] = (h ? x1[j] : x0[j]) / den;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[h] |= e2m1_rne_sat(tq[j]) << (4 * j);
       }
     }
-    if (ok) {
+    if (ok && live) {
       // chunk-major: codes[K/64][M][32 bytes], scales[K/64][M][4]
       uint32_t* cp = reinterpret_cast<uint32_t*>(codes + (int64_t(g) * M + row) * 32);
       cp[q] = w[0];
@@ -245,8 +421,16 @@ __global__ __launch_bounds__(256) void act_quant_nvfp4_kernel(
         sp[2 + (q >> 1)] = uint8_t(sb[1]);
       }
     }
-    lr_mfma<RB>(acc, b0, down, K, r, k0);
-    lr_mfma<RB>(acc, b1, down, K, r, k1);
+    if constexpr (RB <= RB_PREFETCH) {
+      lr_mfma_pre<RB>(acc, b0, dring[sl], 0);
+      lr_mfma_pre<RB>(acc, b1, dring[sl], 1);
+    } else {
+      lr_mfma<RB>(acc, b0, down, K, r, k0);
+      lr_mfma<RB>(acc, b1, down, K, r, k1);
+    }
+    // the slot is free: refill it with the group DEPTH steps ahead
+    fetch(t + DEPTH, sl);
+    }
   }
   lr_reduce_store<RB>(acc, red, row0, M, LR);
 }
@@ -267,9 +451,13 @@ struct Int4Launch {
                         const uint16_t* down, uint8_t* codes, float* scales, uint16_t* LR,
                         hipStream_t s) {
     const size_t shm = RB > 0 ? size_t(WAVES) * ROWS * RB * 16 * sizeof(float) : 0;
+    if (shm > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_int4_kernel<RB, XF32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
+      return svdq::fail(SVDQ_ERR_HIP, "act_quant_int4: shared memory size");
     dim3 grid((M + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((act_quant_int4_kernel<RB, XF32>), grid, dim3(256), shm, s, X, M, K,
-                       smooth, down, codes, scales, LR);
+    hipLaunchKernelGGL((act_quant_int4_kernel<RB, XF32>), grid, dim3(64 * WAVES), shm, s, X, M,
+                       K, smooth, down, codes, scales, LR);
     return svdq::check_launch("act_quant_int4");
   }
 };
@@ -280,9 +468,13 @@ struct Fp4Launch {
                         const uint16_t* down, const float* ts_x, uint8_t* codes,
                         uint8_t* scales, uint16_t* LR, hipStream_t s) {
     const size_t shm = RB > 0 ? size_t(WAVES) * ROWS * RB * 16 * sizeof(float) : 0;
+    if (shm > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_nvfp4_kernel<RB, XF32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
+      return svdq::fail(SVDQ_ERR_HIP, "act_quant_nvfp4: shared memory size");
     dim3 grid((M + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((act_quant_nvfp4_kernel<RB, XF32>), grid, dim3(256), shm, s, X, M,
-                       K, smooth, down, ts_x, codes, scales, LR);
+    hipLaunchKernelGGL((act_quant_nvfp4_kernel<RB, XF32>), grid, dim3(64 * WAVES), shm, s, X,
+                       M, K, smooth, down, ts_x, codes, scales, LR);
     return svdq::check_launch("act_quant_nvfp4");
   }
 };

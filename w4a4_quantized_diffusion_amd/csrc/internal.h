@@ -120,18 +120,17 @@ __device__ __forceinline__ uint32_t e2m1_rne_sat(float t) {
   return (t < 0.f && i != 0) ? (i | 8u) : i;
 }
 
-// rne-to-E2M1 of fl32(z / den): the grid midpoints are exact binary32 values,
-// so only a quotient within 2^-19 (relative to 8) of one can depend on the
-// last bits; those repeat the exact division.
-__device__ __forceinline__ uint32_t e2m1_quot(float z, float den, float inv, bool fast) {
-  float t = z * inv;
+// rne-to-E2M1 of fl32(z / den) from t = z fl32(1/den): the grid midpoints are
+// exact binary32 values, so only a t within 2^-18 of one can round
+// differently from the correctly rounded quotient; those repeat the exact
+// division.
+__device__ __forceinline__ bool e2m1_near_mid(float t) {
   const float a = fabsf(t);
   const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.f};
-  bool near = !fast;
+  bool near = false;
 #pragma unroll
   for (int i = 0; i < 7; ++i) near |= fabsf(a - mids[i]) <= 0x1p-18f;
-  if (near) t = z / den;
-  return e2m1_rne_sat(t);
+  return near;
 }
 
 }  // namespace svdq_dev
