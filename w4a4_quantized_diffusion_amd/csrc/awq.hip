@@ -19,10 +19,11 @@
 //    dequantize straight into the B operand of v_mfma_f32_16x16x32_bf16 in
 //    registers (no LDS staging), one 16-row tile of X at a time, then reduce
 //    their partial sums through LDS in a fixed order.
-//  * larger M: 256 x 256 workgroup tiles, 4 waves of 128 x 128 on
-//    v_mfma_f32_32x32x16_bf16.  Per 64-wide K chunk each thread copies one X
-//    row (bf16, 128 bytes) and dequantizes one weight row into the LDS buffer
-//    the MFMAs are not reading, one chunk ahead; one barrier per chunk.
+//  * larger M: 256 x 256 workgroup tiles, 8 waves (two per SIMD) of 128 x 64
+//    on v_mfma_f32_32x32x16_bf16.  Per 64-wide K chunk each thread either
+//    copies one X row (bf16, 128 bytes) or dequantizes one weight row into
+//    the LDS buffer the MFMAs are not reading, one chunk ahead; one barrier
+//    per chunk.
 
 #include "internal.h"
 
@@ -152,16 +153,16 @@ __global__ __launch_bounds__(SK_NT) void awq_skinny_kernel(
 // ------------------------------------------------------------ large M
 
 constexpr int BM = 256, BN = 256;
-constexpr int NT = 256;
-constexpr int WM = 128, WN = 128;
+constexpr int NT = 512;
+constexpr int WM = 128, WN = 64;
 constexpr int RBL = WM / 32, CBL = WN / 32;
 constexpr int ROWB = 144;               // 64 bf16 values (128 bytes) + 16 pad
 constexpr int STAGE = (BM + BN) * ROWB;
 
+// One staged row's K chunk: an A row's 64 bf16 of X (x0..x7), or a B row's
+// 64 nibbles (x0, x1) with its scale and -zero*scale (x2.x, x2.y).
 struct Chunk {
-  uint4 x0, x1, x2, x3, x4, x5, x6, x7;   // 64 bf16 of the A row
-  uint4 w0, w1;                           // 64 nibbles of the B row
-  float s, zs;
+  uint4 x0, x1, x2, x3, x4, x5, x6, x7;
 };
 
 // 16-byte piece I of the staged A row (I a compile-time constant)
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(NT) void awq_gemm_kernel(
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, r32 = lane & 31;
 
   // XCD-aware tile order, M fastest (workgroups are dealt round-robin to the
@@ -196,38 +197,47 @@ __global__ __launch_bounds__(NT) void awq_gemm_kernel(
   const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
   const int G = K / 64;
 
-  // thread tid stages A row tid and B row tid; rows past the edge repeat the
-  // last row (their products only reach outputs that are never stored)
-  const int64_t ra = m0 + tid < M ? m0 + tid : M - 1;
-  const int64_t rb = n0 + tid < N ? n0 + tid : N - 1;
+  // staging: waves 0..3 stage the 256 A rows (X), waves 4..7 the 256 B rows
+  // (weights); thread tid owns staged row tid.  Rows past the edge repeat the
+  // last row (their products only reach outputs that are never stored).
+  const bool is_a = wave < 4;
+  const int64_t ra = m0 + (tid & 255) < M ? m0 + (tid & 255) : M - 1;
+  const int64_t rb = n0 + (tid & 255) < N ? n0 + (tid & 255) : N - 1;
   auto load_chunk = [&](int g, Chunk& ch) {
-    const uint4* xp = reinterpret_cast<const uint4*>(X + ra * K + 64 * g);
-    ch.x0 = xp[0];
-    ch.x1 = xp[1];
-    ch.x2 = xp[2];
-    ch.x3 = xp[3];
-    ch.x4 = xp[4];
-    ch.x5 = xp[5];
-    ch.x6 = xp[6];
-    ch.x7 = xp[7];
-    const uint4* wp = reinterpret_cast<const uint4*>(q + (int64_t(g) * N + rb) * 32);
-    ch.w0 = wp[0];
-    ch.w1 = wp[1];
-    ch.s = bf16_to_f32(sc[int64_t(g) * N + rb]);
-    ch.zs = -bf16_to_f32(zr[int64_t(g) * N + rb]) * ch.s;
+    if (is_a) {
+      const uint4* xp = reinterpret_cast<const uint4*>(X + ra * K + 64 * g);
+      ch.x0 = xp[0];
+      ch.x1 = xp[1];
+      ch.x2 = xp[2];
+      ch.x3 = xp[3];
+      ch.x4 = xp[4];
+      ch.x5 = xp[5];
+      ch.x6 = xp[6];
+      ch.x7 = xp[7];
+    } else {
+      const uint4* wp = reinterpret_cast<const uint4*>(q + (int64_t(g) * N + rb) * 32);
+      ch.x0 = wp[0];
+      ch.x1 = wp[1];
+      const float s = bf16_to_f32(sc[int64_t(g) * N + rb]);
+      const float zs = -bf16_to_f32(zr[int64_t(g) * N + rb]) * s;
+      ch.x2 = make_uint4(__float_as_uint(s), __float_as_uint(zs), 0, 0);
+    }
   };
   // quarter P (k 16P .. 16P+15) of a staged chunk into LDS; P is a
   // compile-time constant so the chunk stays in registers
   auto stage_quarter = [&](uint8_t* st, const Chunk& ch, auto PC) {
     constexpr int P = decltype(PC)::value;
-    uint4* da = reinterpret_cast<uint4*>(st + tid * ROWB + P * 32);
-    da[0] = xpiece<2 * P>(ch);
-    da[1] = xpiece<2 * P + 1>(ch);
-    const uint32_t w0 = P == 0 ? ch.w0.x : P == 1 ? ch.w0.z : P == 2 ? ch.w1.x : ch.w1.z;
-    const uint32_t w1 = P == 0 ? ch.w0.y : P == 1 ? ch.w0.w : P == 2 ? ch.w1.y : ch.w1.w;
-    uint4* db = reinterpret_cast<uint4*>(st + (BM + tid) * ROWB + P * 32);
-    db[0] = dequant8(w0, ch.s, ch.zs);
-    db[1] = dequant8(w1, ch.s, ch.zs);
+    uint4* d = reinterpret_cast<uint4*>(st + tid * ROWB + P * 32);
+    if (is_a) {
+      d[0] = xpiece<2 * P>(ch);
+      d[1] = xpiece<2 * P + 1>(ch);
+    } else {
+      const uint32_t w0 = P == 0 ? ch.x0.x : P == 1 ? ch.x0.z : P == 2 ? ch.x1.x : ch.x1.z;
+      const uint32_t w1 = P == 0 ? ch.x0.y : P == 1 ? ch.x0.w : P == 2 ? ch.x1.y : ch.x1.w;
+      const float s = __uint_as_float(ch.x2.x), zs = __uint_as_float(ch.x2.y);
+      d[0] = dequant8(w0, s, zs);
+      d[1] = dequant8(w1, s, zs);
+    }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;

@@ -24,12 +24,12 @@
 //  * The epilogue multiplies by ts_x ts_w, adds LR . lora_up^T (bf16 MFMAs,
 //    fp32 accumulation) and the bias, and converts.
 //
-// Tiles: workgroup 256 x 256, 4 waves (one per SIMD) as 2 x 2, each wave
-// 128 x 128 = 4 x 4 blocks of 32 x 32.  Per K chunk a thread loads the packed
-// 32 bytes and 4 block scales of one A row and one B row (chunk-major layout,
-// so the loads of a workgroup are contiguous) one chunk ahead, decodes them
-// into the LDS buffer the MFMAs do not read, and one barrier per chunk swaps
-// the buffers.
+// Tiles: workgroup 256 x 256, 8 waves (two per SIMD) as 2 x 4, each wave
+// 128 x 64 = 4 x 2 blocks of 32 x 32.  Per K chunk a thread loads the packed
+// 32 bytes and 4 block scales of one staged row (chunk-major layout, so the
+// loads of a workgroup are contiguous) one chunk ahead, decodes them into the
+// LDS buffer the MFMAs do not read, and one barrier per chunk swaps the
+// buffers.
 
 #include "internal.h"
 
@@ -40,8 +40,8 @@ namespace {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256;
-constexpr int NT = 256;
-constexpr int WM = 128, WN = 128;
+constexpr int NT = 512;
+constexpr int WM = 128, WN = 64;
 constexpr int RBL = WM / 32, CBL = WN / 32;
 constexpr int ROWB = 144;               // 64 fp16 values (128 bytes) + 16 pad
 constexpr int STAGE = (BM + BN) * ROWB;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, r32 = lane & 31;
 
   // XCD-aware tile order (workgroups are dealt round-robin to the 8 XCDs):
@@ -110,20 +110,21 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
   const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
   const int G = K / 64;
 
-  // staging: thread tid owns A row tid and B row tid of the tile; rows past
-  // the edge repeat the last row (their products reach only accumulator
-  // rows / columns that are never stored)
-  const int64_t ra = m0 + tid < M ? m0 + tid : M - 1;
-  const int64_t rb = n0 + tid < N ? n0 + tid : N - 1;
-  auto load_chunk = [&](int g, PackedRow& pa, PackedRow& pb) {
-    const uint4* ca = reinterpret_cast<const uint4*>(A + (int64_t(g) * M + ra) * 32);
-    const uint4* cb = reinterpret_cast<const uint4*>(W + (int64_t(g) * N + rb) * 32);
-    pa.c0 = ca[0];
-    pa.c1 = ca[1];
-    pb.c0 = cb[0];
-    pb.c1 = cb[1];
-    pa.sb = *reinterpret_cast<const uint32_t*>(sA + (int64_t(g) * M + ra) * 4);
-    pb.sb = *reinterpret_cast<const uint32_t*>(sW + (int64_t(g) * N + rb) * 4);
+  // staging: waves 0..3 stage the 256 A rows of the tile, waves 4..7 the 256
+  // B rows; thread tid owns staged row tid (A row tid, or B row tid - 256).
+  // Rows past the edge repeat the last row (their products reach only
+  // accumulator rows / columns that are never stored).
+  const bool is_a = wave < 4;
+  const int rows_total = is_a ? M : N;
+  const int64_t r0 = (is_a ? m0 : n0) + (tid & 255);
+  const int64_t srow = r0 < rows_total ? r0 : rows_total - 1;
+  const uint8_t* const cbase = is_a ? A : W;
+  const uint8_t* const sbase = is_a ? sA : sW;
+  auto load_chunk = [&](int g, PackedRow& pr) {
+    const uint4* c = reinterpret_cast<const uint4*>(cbase + (int64_t(g) * rows_total + srow) * 32);
+    pr.c0 = c[0];
+    pr.c1 = c[1];
+    pr.sb = *reinterpret_cast<const uint32_t*>(sbase + (int64_t(g) * rows_total + srow) * 4);
   };
   // decode one packed row (dword pair p: codes 16p .. 16p + 15, block p)
   auto decode_pair = [&](uint8_t* row, const PackedRow& pr, int p) {
@@ -143,17 +144,11 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  PackedRow pa[2], pb[2];
-  load_chunk(0, pa[0], pb[0]);
-  if (G > 1) load_chunk(1, pa[1], pb[1]);
-  {
-    uint8_t* st = lds;
+  PackedRow pa[2];
+  load_chunk(0, pa[0]);
+  if (G > 1) load_chunk(1, pa[1]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      decode_pair(st + tid * ROWB, pa[0], p);
-      decode_pair(st + (BM + tid) * ROWB, pb[0], p);
-    }
-  }
+  for (int p = 0; p < 4; ++p) decode_pair(lds + tid * ROWB, pa[0], p);
   __syncthreads();
 
   // fragment offsets inside a stage: A row block i, B row block j, k substep
@@ -165,8 +160,7 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
   // those of ks multiply), the next chunk (packed in na / nb) decoded into
   // stage `nx` a block at a time in between, then the chunk after next
   // fetched into fa_ / fb_ (whose contents were decoded the previous step).
-  auto step = [&](int g, const uint8_t* st, uint8_t* nx, const PackedRow& na,
-                  const PackedRow& nb, PackedRow& fa_, PackedRow& fb_)
+  auto step = [&](int g, const uint8_t* st, uint8_t* nx, const PackedRow& na, PackedRow& fa_)
                   __attribute__((always_inline)) {
     v4i fa[2][RBL], fb[2][CBL];
     auto frags = [&](int ks, v4i (&a)[RBL], v4i (&b)[CBL]) {
@@ -189,21 +183,18 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               __builtin_bit_cast(v8h, fa[ks & 1][i]), __builtin_bit_cast(v8h, fb[ks & 1][j]),
               acc[i][j], 0, 0, 0);
-      if (more) {
-        decode_pair(nx + tid * ROWB, na, ks);
-        decode_pair(nx + (BM + tid) * ROWB, nb, ks);
-      }
+      if (more) decode_pair(nx + tid * ROWB, na, ks);
     }
-    if (g + 2 < G) load_chunk(g + 2, fa_, fb_);
+    if (g + 2 < G) load_chunk(g + 2, fa_);
     __syncthreads();
   };
 
   int g = 0;
   for (; g + 1 < G; g += 2) {
-    step(g, lds, lds + STAGE, pa[1], pb[1], pa[0], pb[0]);
-    step(g + 1, lds + STAGE, lds, pa[0], pb[0], pa[1], pb[1]);
+    step(g, lds, lds + STAGE, pa[1], pa[0]);
+    step(g + 1, lds + STAGE, lds, pa[0], pa[1]);
   }
-  if (g < G) step(g, lds, lds + STAGE, pa[1], pb[1], pa[0], pb[0]);
+  if (g < G) step(g, lds, lds + STAGE, pa[1], pa[0]);
 
   // ------------------------------------------------ epilogue
   const float ts = ts_x[0] * ts_w[0];
