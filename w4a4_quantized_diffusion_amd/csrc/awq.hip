@@ -15,7 +15,8 @@
 //
 // Two kernels:
 //  * M <= 64 (decode-style calls): the layer is bound by reading the 4-bit
-//    weights.  A workgroup owns 32 output columns; its 4 waves split K and
+//    weights.  A workgroup owns 48 output columns (N / 48 workgroups: one
+//    per CU at N = 12288); its 8 waves split K and
 //    dequantize straight into the B operand of v_mfma_f32_16x16x32_bf16 in
 //    registers (no LDS staging), one 16-row tile of X at a time, then reduce
 //    their partial sums through LDS in a fixed order.
@@ -65,75 +66,143 @@ __device__ __forceinline__ void store_y(void* Y, bool ybf16, int64_t idx, float 
 
 // ------------------------------------------------------------ M <= 64
 
-constexpr int SK_NT = 256;     // 4 waves
-constexpr int SK_COLS = 32;    // output columns per workgroup (2 tiles of 16)
+constexpr int SK_WAVES = 8;
+constexpr int SK_NT = 64 * SK_WAVES;
+constexpr int SK_COLS = 48;    // output columns per workgroup (three 16-column tiles)
+constexpr int SK_TILES = SK_COLS / 16;
+
+// The loads of one K chunk for one lane: 8 weight bytes of each of the two
+// column tiles, their scales and zero points, and X for each 16-row tile.
+template <int MT>
+struct SkinnySlot {
+  uint2 wq[SK_TILES];
+  uint32_t sz[SK_TILES];         // bf16 scale | bf16 zero << 16
+  uint4 x[MT][2];
+};
 
 template <int MT>
 __global__ __launch_bounds__(SK_NT) void awq_skinny_kernel(
     const uint16_t* __restrict__ X, int M, int K, int N, const uint8_t* __restrict__ q,
     const uint16_t* __restrict__ sc, const uint16_t* __restrict__ zr,
     const uint16_t* __restrict__ bias, void* __restrict__ Y, bool ybf16) {
-  __shared__ float red[4][MT][2][4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float red[SK_WAVES / 2][MT][SK_TILES][4][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane >> 4, r = lane & 15;
   const int64_t n0 = int64_t(blockIdx.x) * SK_COLS;
   const int G = K / 64;
+  // chunks per slot ring: deep for one 16-row tile, shallower for more
+  constexpr int D = MT == 1 ? 6 : (MT == 2 ? 4 : 2);
 
-  v4f acc[MT][2];
+  v4f acc[MT][SK_TILES];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) acc[mt][t] = v4f{0, 0, 0, 0};
+    for (int t = 0; t < SK_TILES; ++t) acc[mt][t] = v4f{0, 0, 0, 0};
 
   // B operand slot (j, i) of the MFMA for K half h is k = 16 j + 8 h + i, so
   // lane (j, r) of tile t dequantizes bytes 8j .. 8j+7 of row n0 + 16t + r:
   // one 8-byte load per tile and chunk.  The A operand uses the same k map.
-  for (int c = wave; c < G; c += 4) {
-    uint2 wq[2];
-    float s[2], zs[2];
+  // Wave w takes chunks w, w + 8, ...; every slot is always (re)loaded (past
+  // the last chunk with the last chunk's data, rows past M with row M-1) so
+  // that the loads stay in flight in order and the wait counts stay exact.
+  int64_t ncl[SK_TILES];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t n = n0 + 16 * t + r;
-      const int64_t nc = n < N ? n : N - 1;
-      wq[t] = *reinterpret_cast<const uint2*>(q + (int64_t(c) * N + nc) * 32 + 8 * j);
-      s[t] = bf16_to_f32(sc[int64_t(c) * N + nc]);
-      zs[t] = -bf16_to_f32(zr[int64_t(c) * N + nc]) * s[t];
-    }
-    uint4 b[2][2];
+  for (int t = 0; t < SK_TILES; ++t) {
+    const int64_t n = n0 + 16 * t + r;
+    ncl[t] = n < N ? n : N - 1;
+  }
+  int mcl[MT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      b[t][0] = dequant8(wq[t].x, s[t], zs[t]);
-      b[t][1] = dequant8(wq[t].y, s[t], zs[t]);
+  for (int mt = 0; mt < MT; ++mt) mcl[mt] = 16 * mt + r < M ? 16 * mt + r : M - 1;
+  const int T = (G - wave + SK_WAVES - 1) / SK_WAVES;
+  SkinnySlot<MT> ring[D];
+  auto fetch = [&](int tt, SkinnySlot<MT>& sl) __attribute__((always_inline)) {
+    const int c = wave + SK_WAVES * (tt < T ? tt : T - 1);
+#pragma unroll
+    for (int t = 0; t < SK_TILES; ++t) {
+      sl.wq[t] = *reinterpret_cast<const uint2*>(q + (int64_t(c) * N + ncl[t]) * 32 + 8 * j);
+      sl.sz[t] = uint32_t(sc[int64_t(c) * N + ncl[t]]) |
+                 (uint32_t(zr[int64_t(c) * N + ncl[t]]) << 16);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = 16 * mt + r;
-      uint4 a[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-      if (m < M) {
-        const uint4* xp = reinterpret_cast<const uint4*>(X + int64_t(m) * K + 64 * c + 16 * j);
-        a[0] = xp[0];
-        a[1] = xp[1];
+      const uint4* xp = reinterpret_cast<const uint4*>(X + int64_t(mcl[mt]) * K + 64 * c + 16 * j);
+      sl.x[mt][0] = xp[0];
+      sl.x[mt][1] = xp[1];
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) fetch(d, ring[d]);
+  for (int t0 = 0; t0 < T; t0 += D)
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int tt = t0 + d;
+      const bool live = tt < T;
+      SkinnySlot<MT>& sl = ring[d];
+      uint4 b[SK_TILES][2];
+#pragma unroll
+      for (int t = 0; t < SK_TILES; ++t) {
+        const float s = live ? __uint_as_float(sl.sz[t] << 16) : 0.f;
+        const float zs = -__uint_as_float(sl.sz[t] & 0xFFFF0000u) * s;
+        b[t][0] = dequant8(sl.wq[t].x, s, zs);
+        b[t][1] = dequant8(sl.wq[t].y, s, zs);
       }
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int mt = 0; mt < MT; ++mt) {
+        // rows past M carry row M-1's values into output rows never stored
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(v8bf, a[hh]), __builtin_bit_cast(v8bf, b[t][hh]), acc[mt][t],
-              0, 0, 0);
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int t = 0; t < SK_TILES; ++t)
+            acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, sl.x[mt][hh]), __builtin_bit_cast(v8bf, b[t][hh]),
+                acc[mt][t], 0, 0, 0);
+      }
+      fetch(tt + D, sl);
     }
-  }
+  // fixed-order reduction of the 8 waves' partial sums through LDS:
+  // waves 4..7 into 0..3, then 1..3 into 0
+  auto put = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < SK_TILES; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][mt][t][e][lane] = acc[mt][t][e];
+        for (int e = 0; e < 4; ++e) red[slot][mt][t][e][lane] = acc[mt][t][e];
+  };
+  auto add = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < SK_TILES; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mt][t][e] += red[slot][mt][t][e][lane];
+  };
+  if (wave >= 4) put(wave - 4);
+  __syncthreads();
+  if (wave < 4) add(wave);
+  __syncthreads();
+  if (wave >= 1 && wave < 4) put(wave - 1);
   __syncthreads();
   if (wave != 0) return;
+  {
+    v4f s1[MT][SK_TILES];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < SK_TILES; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s1[mt][t][e] = red[0][mt][t][e][lane] + (red[1][mt][t][e][lane] + red[2][mt][t][e][lane]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < SK_TILES; ++t) acc[mt][t] += s1[mt][t];
+  }
   // 16x16 f32 MFMA result: lane l holds column l%16, rows 4(l/16) + e
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < SK_TILES; ++t) {
     const int64_t n = n0 + 16 * t + r;
     if (n >= N) continue;
     const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
@@ -142,10 +211,7 @@ __global__ __launch_bounds__(SK_NT) void awq_skinny_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * mt + 4 * j + e;
-        if (m >= M) continue;
-        const float v = ((red[0][mt][t][e][lane] + red[1][mt][t][e][lane]) +
-                         (red[2][mt][t][e][lane] + red[3][mt][t][e][lane])) + bv;
-        store_y(Y, ybf16, int64_t(m) * N + n, v);
+        if (m < M) store_y(Y, ybf16, int64_t(m) * N + n, acc[mt][t][e] + bv);
       }
   }
 }
@@ -304,20 +370,18 @@ __global__ __launch_bounds__(NT) void awq_gemm_kernel(
   }
   if (g < G) step(g, lds, lds + STAGE, ch1, ch0);
 
-  // 32x32 f32 MFMA result: lane l holds column l%32, rows 8(e/4) + 4(l/32) + e%4
+  // bias, convert, store through each wave's slice of the (now free) stages
+  float bv[CBL];
 #pragma unroll
   for (int jj = 0; jj < CBL; ++jj) {
     const int64_t n = n0 + wn * WN + jj * 32 + r32;
-    if (n >= N) continue;
-    const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
-#pragma unroll
-    for (int i = 0; i < RBL; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < M) store_y(Y, ybf16, m * N + n, acc[i][jj][e] + bv);
-      }
+    bv[jj] = (bias && n < N) ? bf16_to_f32(bias[n]) : 0.f;
   }
+  float* const eb = reinterpret_cast<float*>(lds + wave * (32 * (WN + 4) * 4));
+  if (ybf16)
+    store_wave_tile<RBL, CBL, true>(acc, bv, eb, lane, m0 + wm * WM, n0 + wn * WN, M, N, Y);
+  else
+    store_wave_tile<RBL, CBL, false>(acc, bv, eb, lane, m0 + wm * WM, n0 + wn * WN, M, N, Y);
 }
 
 }  // namespace

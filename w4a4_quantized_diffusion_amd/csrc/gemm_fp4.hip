@@ -197,49 +197,50 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
   if (g < G) step(g, lds, lds + STAGE, pa[1], pa[0]);
 
   // ------------------------------------------------ epilogue
+  // acc * ts_x ts_w, then LR . lora_up^T accumulated on top with bf16 MFMAs
   const float ts = ts_x[0] * ts_w[0];
 #pragma unroll
-  for (int j = 0; j < CBL; ++j) {
-    const int64_t n = n0 + wn * WN + j * 32 + r32;
-    const int64_t nc = n < N ? n : N - 1;
-    const float bv = bias ? (BBF16 ? load_bias<uint16_t>(bias, nc) : load_bias<float>(bias, nc))
-                          : 0.f;
+  for (int i = 0; i < RBL; ++i)
 #pragma unroll
-    for (int i = 0; i < RBL; ++i) {
-      v16f lr;
+    for (int j = 0; j < CBL; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lr[e] = 0.f;
-      if constexpr (RK > 0) {
-        const int R = RK * 16;
-        const int64_t rr = m0 + wm * WM + i * 32 + r32;
-        const int64_t rc = rr < M ? rr : M - 1;
+      for (int e = 0; e < 16; ++e) acc[i][j][e] *= ts;
+  if constexpr (RK > 0) {
+    const int R = RK * 16;
 #pragma unroll
-        for (int kk = 0; kk < RK; ++kk) {
-          const int kof = kk * 16 + h * 8;
-          const uint4 la = *reinterpret_cast<const uint4*>(LR + rc * R + kof);
-          const uint4 u = *reinterpret_cast<const uint4*>(up + nc * R + kof);
-          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(v8bf, v4i{int(la.x), int(la.y), int(la.z), int(la.w)}),
-              __builtin_bit_cast(v8bf, v4i{int(u.x), int(u.y), int(u.z), int(u.w)}), lr, 0, 0,
-              0);
-        }
+    for (int kk = 0; kk < RK; ++kk) {
+      const int kof = kk * 16 + h * 8;
+      v4i ub[CBL];
+#pragma unroll
+      for (int j = 0; j < CBL; ++j) {
+        const int64_t nb = n0 + wn * WN + j * 32 + r32;
+        const int64_t nc = nb < N ? nb : N - 1;
+        const uint4 u = *reinterpret_cast<const uint4*>(up + nc * R + kof);
+        ub[j] = v4i{int(u.x), int(u.y), int(u.z), int(u.w)};
       }
-      // 32x32 f32 MFMA result: lane l holds column l%32, rows 8(e/4) + 4(l/32) + e%4
-      if (n < N) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t m = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (m < M) {
-            const float v = acc[i][j][e] * ts + lr[e] + bv;
-            if (YBF16)
-              static_cast<uint16_t*>(Y)[m * N + n] = f32_to_bf16(v);
-            else
-              static_cast<float*>(Y)[m * N + n] = v;
-          }
-        }
+      for (int i = 0; i < RBL; ++i) {
+        const int64_t ra = m0 + wm * WM + i * 32 + r32;
+        const int64_t rc = ra < M ? ra : M - 1;
+        const uint4 la = *reinterpret_cast<const uint4*>(LR + rc * R + kof);
+        const v4i lai = {int(la.x), int(la.y), int(la.z), int(la.w)};
+#pragma unroll
+        for (int j = 0; j < CBL; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(v8bf, lai), __builtin_bit_cast(v8bf, ub[j]), acc[i][j], 0, 0, 0);
       }
     }
   }
+  // bias, convert, store through each wave's slice of the (now free) stages
+  float bv[CBL];
+#pragma unroll
+  for (int j = 0; j < CBL; ++j) {
+    const int64_t n = n0 + wn * WN + j * 32 + r32;
+    bv[j] = (bias && n < N) ? (BBF16 ? load_bias<uint16_t>(bias, n) : load_bias<float>(bias, n))
+                            : 0.f;
+  }
+  float* const eb = reinterpret_cast<float*>(lds + wave * (32 * (WN + 4) * 4));
+  store_wave_tile<RBL, CBL, YBF16>(acc, bv, eb, lane, m0 + wm * WM, n0 + wn * WN, M, N, Y);
 }
 
 template <int RK>

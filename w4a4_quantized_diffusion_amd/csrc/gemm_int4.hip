@@ -447,8 +447,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   // wave instead passes one 32-row block row at a time through a private LDS
   // buffer (the stages are free now) and stores whole 16-byte row pieces.
   __syncthreads();
-  constexpr int ER = WN + 4;                 // floats per LDS row (padded)
-  constexpr int EBYTES = 32 * ER * 4;        // one block row of one wave
+  constexpr int EBYTES = 32 * (WN + 4) * 4;  // one block row of one wave
   static_assert(6 * EBYTES <= int(sizeof(Stage)) && 2 * EBYTES <= int(sizeof(Stage)),
                 "epilogue buffers must fit in the stages");
   float* const eb = reinterpret_cast<float*>(
@@ -461,47 +460,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     bv[j] = (bias && n < N) ? (BBF16 ? load_bias<uint16_t>(bias, n) : load_bias<float>(bias, n))
                             : 0.f;
   }
-  const int64_t col0 = n0 + wn * WN;
-#pragma unroll
-  for (int i = 0; i < RBL; ++i) {
-#pragma unroll
-    for (int j = 0; j < CBL; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        eb[(8 * (e >> 2) + 4 * h + (e & 3)) * ER + j * 32 + r32] = acc[i][j][e] + bv[j];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int64_t row0 = m0 + wm * WM + i * 32;
-    if (YBF16) {
-      // lane: rows lane/8 + 8t, columns 8 (lane%8) .. +8
-      const int q = lane & 7;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int rr = (lane >> 3) + 8 * t;
-        const float4 a = *reinterpret_cast<const float4*>(eb + rr * ER + 8 * q);
-        const float4 b = *reinterpret_cast<const float4*>(eb + rr * ER + 8 * q + 4);
-        const int64_t m = row0 + rr, n = col0 + 8 * q;
-        if (m < M && n < N)
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + m * N + n) =
-              make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                         pack_bf16x2(b.z, b.w));
-      }
-    } else {
-      // lane: rows lane/16 + 4t, columns 4 (lane%16) .. +4
-      const int q = lane & 15;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int rr = (lane >> 4) + 4 * t;
-        const float4 a = *reinterpret_cast<const float4*>(eb + rr * ER + 4 * q);
-        const int64_t m = row0 + rr, n = col0 + 4 * q;
-        if (m < M && n < N) *reinterpret_cast<float4*>(static_cast<float*>(Y) + m * N + n) = a;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
+  store_wave_tile<RBL, CBL, YBF16>(acc, bv, eb, lane, m0 + wm * WM, n0 + wn * WN, M, N, Y);
 }
 
 

@@ -133,4 +133,62 @@ __device__ __forceinline__ bool e2m1_near_mid(float t) {
   return near;
 }
 
+// Store one wave's tile of 32x32 f32 MFMA results (RBL x CBL blocks; lane l
+// holds column l%32, rows 8(e/4) + 4(l/32) + e%4 of each block) plus a
+// per-column bias.  One 32-row block row at a time passes through the
+// wave's private LDS buffer `eb` (32 x (32 CBL + 4) floats), so that every
+// lane writes whole 16-byte pieces of output rows instead of 2- or 4-byte
+// scattered elements.  The caller makes `eb` free (no other wave uses it).
+template <int RBL, int CBL, bool YBF16>
+__device__ __forceinline__ void store_wave_tile(const v16f (&acc)[RBL][CBL],
+                                                const float (&bv)[CBL], float* eb, int lane,
+                                                int64_t row0, int64_t col0, int M, int N,
+                                                void* Y) {
+  constexpr int WN = 32 * CBL;
+  constexpr int ER = WN + 4;
+  const int h = lane >> 5, r32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < RBL; ++i) {
+#pragma unroll
+    for (int j = 0; j < CBL; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        eb[(8 * (e >> 2) + 4 * h + (e & 3)) * ER + j * 32 + r32] = acc[i][j][e] + bv[j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t rb = row0 + i * 32;
+    if constexpr (YBF16) {
+      constexpr int CH = WN / 8;                  // 16-byte pieces per row
+      constexpr int RPI = 64 / CH;                // rows per instruction
+      const int q = lane % CH;
+#pragma unroll
+      for (int t = 0; t < 32 / RPI; ++t) {
+        const int rr = lane / CH + RPI * t;
+        const float4 a = *reinterpret_cast<const float4*>(eb + rr * ER + 8 * q);
+        const float4 b = *reinterpret_cast<const float4*>(eb + rr * ER + 8 * q + 4);
+        const int64_t m = rb + rr, n = col0 + 8 * q;
+        if (m < M && n < N)
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + m * N + n) =
+              make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                         pack_bf16x2(b.z, b.w));
+      }
+    } else {
+      constexpr int CH = WN / 4;
+      constexpr int RPI = 64 / CH;
+      const int q = lane % CH;
+#pragma unroll
+      for (int t = 0; t < 32 / RPI; ++t) {
+        const int rr = lane / CH + RPI * t;
+        const float4 a = *reinterpret_cast<const float4*>(eb + rr * ER + 4 * q);
+        const int64_t m = rb + rr, n = col0 + 4 * q;
+        if (m < M && n < N) *reinterpret_cast<float4*>(static_cast<float*>(Y) + m * N + n) = a;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 }  // namespace svdq_dev
