@@ -16,12 +16,12 @@
 //    returns I_g exactly, already as fp32.  Nibbles are widened to E4M3
 //    bytes with a byte-permute table while a tile is staged into LDS.
 //  * The group scale is an outer product sA[:,g] sW[:,g]^T.  The kernel
-//    computes it on the matrix core too: each fp32 scale is split into three
-//    bf16 pieces (hi + mid + lo, exact), and one 32x32x16 bf16 MFMA sums the
-//    nine piece products, giving sA*sW to fp32 accuracy in the same register
-//    layout as I_g.  The vector ALU then does one FMA per element and group:
-//    acc += S (.) I.  (VALU fp32 runs at 16 lanes/clk per SIMD, so two VALU
-//    ops per element-group would bound the kernel at half the FP8 rate.)
+//    forms it on the matrix core too: the two-block 32x32x1 fp32 MFMA gives
+//    fl32(sA sW) for a row block and both column blocks of a wave at once, in
+//    the same register layout as I_g.  The vector ALU then does one FMA per
+//    element and group: acc += S (.) I.  (VALU fp32 issue is the other
+//    limited resource, so the scale product must not cost a second VALU op
+//    per element-group.)
 //  * The epilogue accumulates LR . lora_up^T into the same fp32 tile with
 //    32x32x16 bf16 MFMAs, adds the bias and converts.
 //
@@ -34,6 +34,8 @@
 #include <cstddef>
 
 using namespace svdq_dev;
+
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 namespace {
 
@@ -50,28 +52,15 @@ __device__ __forceinline__ void nib8_to_e4m3(uint32_t w, uint32_t& lo, uint32_t&
   hi = __builtin_amdgcn_perm(T1, T0, so) | (w & 0x80808080u);
 }
 
-// fp32 -> three bf16 pieces whose exact sum is the input (truncation split).
-__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
-  const uint32_t u = __float_as_uint(x);
-  const float fh = __uint_as_float(u & 0xFFFF0000u);
-  const float r1 = x - fh;                         // exact
-  const uint32_t u1 = __float_as_uint(r1);
-  const float fm = __uint_as_float(u1 & 0xFFFF0000u);
-  const float r2 = r1 - fm;                        // exact, fits bf16
-  h = u >> 16;
-  m = u1 >> 16;
-  l = __float_as_uint(r2) >> 16;
-}
-
 // --------------------------------------------------------------- tiling
 //
 // Workgroup tile 256 x 256, 8 waves (2 per SIMD) arranged 2 (M) x 4 (N), each
 // wave 128 x 64 = 4 x 2 blocks of 32 x 32 (128 fp32 accumulators per lane,
 // in VGPRs so the vector ALU can apply the group scales).  One K-group (64
 // codes) per pipeline step: while the waves run the MFMAs of group g out of
-// one LDS buffer, they widen the packed codes of group g+1 (already in
-// registers) into the other buffer and issue the global loads of group g+2.
-// One barrier per group.  LDS rows are padded to 80 bytes so that the 16
+// one LDS buffer, they widen the packed codes of group g+1 (DMA'd into LDS one
+// step earlier) into the other buffer and start the DMA of group g+2.  One
+// barrier per group.  LDS rows are padded to 80 bytes so that the 16
 // lanes of one ds_read_b128 phase (16 consecutive rows) hit distinct banks.
 
 constexpr int BM = 256, BN = 256;
@@ -83,8 +72,8 @@ constexpr int LDS_ROW = 80;             // 64 bytes of E4M3 codes + 16 pad
 struct Stage {
   uint8_t a[BM * LDS_ROW];
   uint8_t b[BN * LDS_ROW];
-  uint4 sa[2][BM];                      // scale pieces, A operand, per k-slot half
-  uint4 sb[2][BN];                      // scale pieces, B operand, per k-slot half
+  float sa[BM];                         // group scales of the A rows
+  float sb[BN];                         // group scales of the B rows
 };
 
 // Packed codes and scales of one group, fetched global -> LDS by DMA.  Each
@@ -150,19 +139,6 @@ __device__ __forceinline__ void unpack_row(const uint4& p0, const uint4& p1, uin
   d[3] = make_uint4(o[12], o[13], o[14], o[15]);
 }
 
-// The scale of one row / column, split into bf16 pieces and laid out as the
-// two k-slot halves of a 32x32x16 bf16 MFMA operand.  Slot pairs (A x B):
-// (h,h) (h,m) (h,l) (m,h) (m,m) (m,l) (l,h) (l,m) in half 0, (l,l) in half 1.
-__device__ __forceinline__ void scale_pieces(float s, bool a_side, uint4& half0, uint4& half1) {
-  uint32_t h, m, l;
-  split3(s, h, m, l);
-  const uint4 a = make_uint4(h | (h << 16), h | (m << 16), m | (m << 16), l | (l << 16));
-  const uint4 b = make_uint4(h | (m << 16), l | (h << 16), m | (l << 16), h | (m << 16));
-  half0 = make_uint4(a_side ? a.x : b.x, a_side ? a.y : b.y, a_side ? a.z : b.z,
-                     a_side ? a.w : b.w);
-  half1 = make_uint4(l, 0, 0, 0);
-}
-
 template <int RK, bool YBF16, bool BBF16>
 __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA,
@@ -199,7 +175,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   const int rows_total = is_a ? M : N;
   const int64_t row0 = is_a ? m0 : n0;
   const int soff = (is_a ? 0 : int(offsetof(Stage, b))) + srow * LDS_ROW;
-  const int sidx = (is_a ? int(offsetof(Stage, sa)) : int(offsetof(Stage, sb))) + srow * 16;
+  const int sidx = (is_a ? int(offsetof(Stage, sa)) : int(offsetof(Stage, sb))) + srow * 4;
   const uint8_t* const gbase = is_a ? A : W;
   const float* const sbase = is_a ? sA : sW;
   // per-lane byte offsets (within one group's slab) of the two code transfers
@@ -236,7 +212,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(w) : "v"(addr));
   };
   // widen packed word `word` (index w) into 8 E4M3 bytes at LDS offset 8w
-  // LDS stores of the widened codes / scale pieces go through asm as well:
+  // LDS stores of the widened codes / scales go through asm as well:
   // the compiler would wait for every DMA in flight before any LDS store.
   typedef __attribute__((address_space(3))) uint8_t* lds_bptr;
   auto lds_addr = [](void* p) { return uint32_t(reinterpret_cast<uintptr_t>((lds_bptr)p)); };
@@ -276,17 +252,13 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
         break;
     }
   };
-  auto pieces = [&](uint8_t* stage_base, const Packed& pk) {
+  // the staged row's group scale, copied next to the widened codes (the
+  // packed buffer is refilled by DMA while the stage is in use)
+  auto stage_scale = [&](uint8_t* stage_base, const Packed& pk) {
     float sv;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
                  : "=v"(sv) : "v"(lds_addr((void*)&pk.scale[tid])));
-    uint4 p0, p1;
-    scale_pieces(sv, is_a, p0, p1);
-    const v4i q0 = {int(p0.x), int(p0.y), int(p0.z), int(p0.w)};
-    const v4i q1 = {int(p1.x), int(p1.y), int(p1.z), int(p1.w)};
-    const uint32_t a = lds_addr(stage_base + sidx);
-    lds_store_b128<0>(a, q0);
-    lds_store_b128<BM * 16>(a, q1);
+    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(stage_base + sidx)), "v"(sv));
   };
 
   v16f acc[RBL][CBL];
@@ -299,57 +271,56 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   v16f zero;
 #pragma unroll
   for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+  v32f zero32;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) zero32[e] = 0.f;
 
   uint8_t* const stage0 = reinterpret_cast<uint8_t*>(&st0);
   uint8_t* const stage1 = reinterpret_cast<uint8_t*>(&st1);
 
-  // Integer products of two blocks in flight (block b uses P[b & 1]), the
-  // scale outer product of one.
-  v16f P[2], S;
+  // the integer products of one block; the scale outer products of one row
+  // block (both column blocks) in S2
+  v16f P[1];
+  v32f S2;
   v8i fb[CBL], fa;
-  v4i qa, qb[CBL];
+  float qa, qb;
   auto load_b = [&](const Stage& cs) {
 #pragma unroll
     for (int j = 0; j < CBL; ++j) {
       const int rb = wn * WN + j * 32 + r32;
       fb[j] = lds_frag(cs.b + rb * LDS_ROW + h * 32);
-      const uint4 w = cs.sb[h][rb];
-      qb[j] = v4i{int(w.x), int(w.y), int(w.z), int(w.w)};
     }
-  };
-  auto load_qb = [&](const Stage& cs, int j) {
-    const uint4 w = cs.sb[h][wn * WN + j * 32 + r32];
-    return v4i{int(w.x), int(w.y), int(w.z), int(w.w)};
+    qb = cs.sb[wn * WN + lane];       // lane l: column l of the wave tile
   };
   auto load_fa = [&](const Stage& cs, int i) {
     fa = lds_frag(cs.a + (wm * WM + i * 32 + r32) * LDS_ROW + h * 32);
   };
-  auto load_qa = [&](const Stage& cs, int i) {
-    const uint4 w = cs.sa[h][wm * WM + i * 32 + r32];
-    qa = v4i{int(w.x), int(w.y), int(w.z), int(w.w)};
-  };
+  auto load_qa = [&](const Stage& cs, int i) { qa = cs.sa[wm * WM + i * 32 + r32]; };
   auto mfma_p = [&](int b) {          // block b = (i = b / 2, j = b % 2)
-    P[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[b & 1], zero, 0, 0, 0,
+    P[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[b & 1], zero, 0, 0, 0,
                                                               127, 0, 127);
   };
-  auto mfma_s = [&](int b, const v4i& qbj) {
-    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, qa),
-                                                __builtin_bit_cast(v8bf, qbj), zero, 0, 0, 0);
-    (void)b;
-  };
+  // sA (x) sW for the current row block and both column blocks: the
+  // two-block 32x32x1 fp32 MFMA takes rows from lanes 32b + r and columns
+  // from lanes 32b + c for block b, so every lane passes its row's sA and
+  // sW of column l of the wave tile; block j lands in S2[16 j, 16 j + 16)
+  // in the usual 32x32 layout.  Each element is fl32(sA sW).
+  auto mfma_s2 = [&]() { S2 = __builtin_amdgcn_mfma_f32_32x32x1f32(qa, qb, zero32, 0, 0, 0); };
   auto fma_block = [&](int b) {
     const int i = b >> 1, j = b & 1;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(S[e], P[b & 1][e], acc[i][j][e]);
+    for (int e = 0; e < 16; ++e)
+      acc[i][j][e] = fmaf(S2[16 * j + e], P[0][e], acc[i][j][e]);
   };
 
-  // One K-group.  Per block b: the integer-product MFMA of block b+1 is
-  // issued, then the FMAs of block b, then the scale MFMA of block b+1, so
-  // the matrix core always has queued work while the vector ALU applies the
-  // scales.  The FMAs of block 7 run after the barrier, while the next
-  // group's fragments load.  The next group's codes (in registers) are
-  // widened into `nxt` in between; on the last group this fills the idle
-  // buffer with data nobody reads, which keeps the loop body branch-free.
+  // One K-group.  Per block b: the FMAs of block b (their scale products
+  // were formed one or two blocks earlier), the integer-product MFMA of block
+  // b+1, and at each new row block the two-block scale MFMA; the other wave
+  // on the SIMD keeps the matrix core busy while this one waits.  The FMAs of
+  // block 7 run after the barrier, while the next group's fragments load.
+  // The next group's codes are widened into `nxt` in between; on the last
+  // group this fills the idle buffer with data nobody reads, which keeps the
+  // loop body branch-free.
   auto group_step = [&](const uint8_t* cur, uint8_t* nxt, const Packed& pk_next, Packed& pk_free,
                         bool tail, int gdma) {
     const Stage& cs = *reinterpret_cast<const Stage*>(cur);
@@ -357,25 +328,25 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     load_b(cs);
     load_fa(cs, 0);
     load_qa(cs, 0);
-    mfma_p(0);
     if (tail) fma_block(7);             // previous group's last block
-    mfma_s(0, qb[0]);
+    mfma_p(0);
+    mfma_s2();                          // row block 0
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 7; ++b) {
       const bool new_row = (b & 1) == 1;      // block b+1 starts row block (b+1)/2
-      // issue order is fixed with scheduling barriers: the integer MFMA of
-      // block b+1 goes out before the FMAs of block b read the products of
-      // block b, so the two product buffers are live together (distinct
-      // registers) and the FMAs overlap the MFMA instead of waiting for it
+      // issue order is fixed with scheduling barriers.  One product buffer: the FMAs of block b read it before the MFMA of
+      // block b+1 overwrites it; the next row block's fragment and scale
+      // load only after that MFMA has taken the current ones
+      fma_block(b);
       mfma_p(b + 1);
       __builtin_amdgcn_sched_barrier(0);
-      if (!new_row && b + 2 < 8) load_fa(cs, (b + 2) >> 1);
+      if (!new_row && b + 2 < 8) {
+        load_fa(cs, (b + 2) >> 1);
+        load_qa(cs, (b + 2) >> 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      fma_block(b);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_s(b + 1, qb[(b + 1) & 1]);
-      if (!new_row && b + 2 < 8) load_qa(cs, (b + 2) >> 1);
+      if (new_row) mfma_s2();           // row block (b+1)/2, after block b used S2
       if (b == 3) {
         // no fragment load pending here: wait for the previous step's DMA
         // and fetch the first packed words of group g+1
@@ -384,7 +355,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
       }
       if (b == 5) fetch4(pk_next, 1, pw);
       if (b >= 3) widen_pair(nxt, b - 3);
-      if (b == 6) pieces(nxt, pk_next);
+      if (b == 6) stage_scale(nxt, pk_next);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -397,7 +368,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   dma(G > 1 ? 1 : 0, pkb1);
   __builtin_amdgcn_s_waitcnt(0x0F73);    // group 0 landed
   widen_all(stage0, pkb0);
-  pieces(stage0, pkb0);
+  stage_scale(stage0, pkb0);
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("s_barrier" ::: "memory");
 
@@ -448,11 +419,10 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   // buffer (the stages are free now) and stores whole 16-byte row pieces.
   __syncthreads();
   constexpr int EBYTES = 32 * (WN + 4) * 4;  // one block row of one wave
-  static_assert(6 * EBYTES <= int(sizeof(Stage)) && 2 * EBYTES <= int(sizeof(Stage)),
-                "epilogue buffers must fit in the stages");
+  static_assert(4 * EBYTES <= int(sizeof(Stage)), "epilogue buffers must fit in the stages");
   float* const eb = reinterpret_cast<float*>(
-      wave < 6 ? reinterpret_cast<uint8_t*>(&st0) + wave * EBYTES
-               : reinterpret_cast<uint8_t*>(&st1) + (wave - 6) * EBYTES);
+      wave < 4 ? reinterpret_cast<uint8_t*>(&st0) + wave * EBYTES
+               : reinterpret_cast<uint8_t*>(&st1) + (wave - 4) * EBYTES);
   float bv[CBL];
 #pragma unroll
   for (int j = 0; j < CBL; ++j) {
