@@ -3,7 +3,9 @@
 
 One step is one full layer call (svdq_linear_w4a4: the fused activation
 kernel, then the W4xA4 GEMM with its low-rank / bias epilogue) on one batch
-of seeded synthetic activations, inputs resident in HBM.  Workload: the
+of seeded synthetic activations, inputs resident in HBM.  The timed steps
+replay a HIP graph of the same library calls (no host launch gaps); the
+eager per-call loop is timed too and reported beside it.  Workload: the
 FLUX-scale projection M 4096 x K 3072 -> N 12288, rank 32, INT4 groups of 64,
 bf16 activations and output.  Weights are quantized once, offline, by the
 library's own svdq_quantize_weights.
@@ -241,10 +243,36 @@ def main():
         step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
+    # eager: one library call per step from Python
     e0.record()
     for i in range(args.steps):
         step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+
+    # the same steps captured into HIP graphs (one per X / Y buffer) and
+    # replayed: the two kernels per step without host launch gaps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(args.nbuf):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(args.nbuf):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for i in range(args.nbuf):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % args.nbuf].replay()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -289,6 +317,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "pct_of_mfma_peak": round(100.0 * value / PEAK_FP8_TOPS, 2),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
+        "eager_ms_per_step": round(ms_eager, 5),
+        "timing": "HIP graph of the layer's steps replayed (eager per-call loop in eager_ms_per_step)",
         "roofline": {
             "kernel": "gemm_int4_kernel",
             "bound": "mfma",
@@ -313,7 +343,7 @@ def main():
         },
         "gpu": torch.cuda.get_device_name(0),
     }
-    del xs, ys, ws, layer
+    del xs, ys, ws, layer, graphs
     torch.cuda.empty_cache()
     if not args.no_other_paths:
         out["other_paths"] = other_paths(args.other_steps)

@@ -204,3 +204,35 @@ def test_flagship_full_size_sampled_rows():
     y_ref, _ = O.linear_w4a4(x[rows], lay)
     assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, "flagship rows")
     assert_lr_close(lr[torch.from_numpy(rows).cuda()], x[rows], lay["lora_down"], "flagship LR")
+
+
+def test_linear_graph_replay_matches_eager():
+    """The layer captured into a HIP graph (the benchmark replays one): every
+    replay, with eager work and synchronisations in between, gives the eager
+    call's output bit for bit."""
+    s = synth.layer(300, 1024, 272, 32, seed=9, workload="attn")
+    lay = _oracle_layer(s["w"], s["x"], 32)
+    d = layer_to_device(lay, 32, 272, 1024)
+    x = t_x(s["x"], True)
+    bias = torch.from_numpy(s["b"]).to("cuda").to(torch.bfloat16)
+    ws = torch.empty(svdq.svdq_workspace_bytes(300, 1024, 32), dtype=torch.uint8, device="cuda")
+    y_eager = svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_eager)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, Y=y)      # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, Y=y)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {rep} differs from the eager call"
+        svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, y_dtype=torch.bfloat16)   # eager in between
+        torch.cuda.synchronize()
