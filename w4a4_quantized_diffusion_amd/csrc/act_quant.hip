@@ -14,7 +14,7 @@
 //
 // Work split: a workgroup of 8 waves owns 16 rows; wave w takes the K-groups
 // w, w+8, ... so that at every step the 8 waves read adjacent 128-byte
-// pieces of each row, and keeps the X loads of its next 4 groups in flight
+// pieces of each row, and keeps the X loads of its next 3 groups in flight
 // (the kernel is bound by reading X).  Lane l owns row (l % 16) and the two
 // 8-element chunks k = 64g + 8(l/16) + [0, 8) and +32: exactly the A-operand slice of
 // a 16x16x32 bf16 MFMA, so the down-projection needs no data movement.
