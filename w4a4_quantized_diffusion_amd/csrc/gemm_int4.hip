@@ -10,11 +10,13 @@
 // of the aiphreaks.com page, "Technical Breakdown").
 //
 // Mapping to CDNA4:
-//  * Codes in -7..7 are exact FP8-E4M3 values and every partial sum of a
-//    64-long group of their products is an integer below 2^12, so one
-//    v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 = one group, unit scales)
-//    returns I_g exactly, already as fp32.  Nibbles are widened to E4M3
-//    bytes with a byte-permute table while a tile is staged into LDS.
+//  * A code q in -7..7 is exact in FP8-E4M3 as the subnormal q 2^-9 (the
+//    byte is the nibble's magnitude with the sign moved to bit 7, so the
+//    widening is three bit operations per four codes).  Every partial sum of
+//    a 64-long group of products is an integer multiple of 2^-18 below 2^-6,
+//    so one v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 = one group) with E8M0
+//    block scales of 2^9 on both operands returns I_g exactly, already as
+//    fp32.  The nibbles are widened while a tile is staged into LDS.
 //  * The group scale is an outer product sA[:,g] sW[:,g]^T.  The kernel
 //    forms it on the matrix core too: the two-block 32x32x1 fp32 MFMA gives
 //    fl32(sA sW) for a row block and both column blocks of a wave at once, in
@@ -41,16 +43,15 @@ namespace {
 
 // ---------------------------------------------------------------- unpack
 
-// Eight sign-magnitude nibbles (one 32-bit word) -> eight E4M3 bytes.
-// lo: bytes of the even nibbles, hi: bytes of the odd nibbles.
+// Eight sign-magnitude nibbles (one 32-bit word) -> eight E4M3 bytes that
+// hold the codes as subnormals: byte s000 0mmm is (-1)^s m 2^-9.  lo: bytes
+// of the even nibbles, hi: bytes of the odd nibbles.  The MFMA's E8M0 block
+// scales (2^9 on each operand) restore the integer products exactly.
 __device__ __forceinline__ void nib8_to_e4m3(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  // E4M3 encodings of 0..7: 00 38 40 44 | 48 4A 4C 4E
-  constexpr uint32_t T0 = 0x44403800u, T1 = 0x4E4C4A48u;
-  const uint32_t se = w & 0x07070707u;
-  const uint32_t so = (w >> 4) & 0x07070707u;
-  lo = __builtin_amdgcn_perm(T1, T0, se) | ((w << 4) & 0x80808080u);
-  hi = __builtin_amdgcn_perm(T1, T0, so) | (w & 0x80808080u);
+  lo = (w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  hi = ((w >> 4) & 0x07070707u) | (w & 0x80808080u);
 }
+constexpr int CODE_SCALE = 127 + 9;     // E8M0 2^9
 
 // --------------------------------------------------------------- tiling
 //
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   auto load_qa = [&](const Stage& cs, int i) { qa = cs.sa[wm * WM + i * 32 + r32]; };
   auto mfma_p = [&](int b) {          // block b = (i = b / 2, j = b % 2)
     P[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[b & 1], zero, 0, 0, 0,
-                                                              127, 0, 127);
+                                                              CODE_SCALE, 0, CODE_SCALE);
   };
   // sA (x) sW for the current row block and both column blocks: the
   // two-block 32x32x1 fp32 MFMA takes rows from lanes 32b + r and columns
