@@ -339,7 +339,12 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
       // issue order is fixed with scheduling barriers.  One product buffer: the FMAs of block b read it before the MFMA of
       // block b+1 overwrites it; the next row block's fragment and scale
       // load only after that MFMA has taken the current ones
+      // the FMAs issue at raised wave priority, so that of the two waves on
+      // a SIMD the one with vector work ready goes first and the other's
+      // MFMA issue slips behind it: the pair drifts out of step
+      __builtin_amdgcn_s_setprio(1);
       fma_block(b);
+      __builtin_amdgcn_s_setprio(0);
       mfma_p(b + 1);
       __builtin_amdgcn_sched_barrier(0);
       if (!new_row && b + 2 < 8) {
