@@ -239,7 +239,9 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
   // group's data, so that the ring keeps fixed registers and its loads stay
   // in flight
   auto fetch = [&](int tt, int sl_) __attribute__((always_inline)) {
-    const int gg = wave + WAVES * (tt < T ? tt : T - 1);
+    // (a wave with no group at all, T = 0, loads group 0 and never uses it)
+    const int tc = tt < T ? tt : T - 1;
+    const int gg = tc >= 0 ? wave + WAVES * tc : 0;
     load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
     load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
     load_down<RB>(down, K, r, gg * 64 + 8 * q, dring[sl_]);
@@ -350,7 +352,9 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
   // group's data, so that the ring keeps fixed registers and its loads stay
   // in flight
   auto fetch = [&](int tt, int sl_) __attribute__((always_inline)) {
-    const int gg = wave + WAVES * (tt < T ? tt : T - 1);
+    // (a wave with no group at all, T = 0, loads group 0 and never uses it)
+    const int tc = tt < T ? tt : T - 1;
+    const int gg = tc >= 0 ? wave + WAVES * tc : 0;
     load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
     load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
     load_down<RB>(down, K, r, gg * 64 + 8 * q, dring[sl_]);
