@@ -118,7 +118,9 @@ __global__ __launch_bounds__(SK_NT) void awq_skinny_kernel(
   const int T = (G - wave + SK_WAVES - 1) / SK_WAVES;
   SkinnySlot<MT> ring[D];
   auto fetch = [&](int tt, SkinnySlot<MT>& sl) __attribute__((always_inline)) {
-    const int c = wave + SK_WAVES * (tt < T ? tt : T - 1);
+    // (a wave with no chunk at all, T = 0, loads chunk 0 and never uses it)
+    const int tc = tt < T ? tt : T - 1;
+    const int c = tc >= 0 ? wave + SK_WAVES * tc : 0;
 #pragma unroll
     for (int t = 0; t < SK_TILES; ++t) {
       sl.wq[t] = *reinterpret_cast<const uint2*>(q + (int64_t(c) * N + ncl[t]) * 32 + 8 * j);
