@@ -74,6 +74,27 @@ def test_nvfp4_act_quant_bf16_ragged_rows(m):
     _check_act(s["x"], _oracle_layer(s["w"], s["x"], 32), 32, bf16=True)
 
 
+def test_nvfp4_act_quant_grid_midpoints():
+    """Block amax 12 with tensor scale 1 gives the block scale 2.0, so the
+    quotients z / 2 are exact: every E2M1 midpoint (0.25 ... 5), one ulp on
+    either side of it, both signs, and the ties that round to zero.  Codes
+    and scales must match the oracle bit for bit."""
+    k, m = 256, 16
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(9))])
+    vals = np.concatenate([vals, -vals]) * np.float32(2.0)     # z = 2 t
+    x = np.zeros((m, k), np.float32)
+    for r in range(m):
+        for b in range(k // 16):
+            x[r, 16 * b] = 12.0 if (r + b) % 2 else -12.0
+            for i in range(1, 16):
+                x[r, 16 * b + i] = vals[(r * 7 + b * 15 + i) % vals.size]
+    lay = dict(smooth=np.ones(k, np.float32), ts_x=np.float32(1.0), ts_w=np.float32(1.0),
+               codes=np.zeros((16, k), np.uint8), sbw=np.zeros((16, k // 16), np.uint8),
+               lora_down=None, lora_up=None)
+    _check_act(x, lay, 0, bf16=False)
+
+
 def _random_e2m1(g, shape):
     """Random E2M1 nibbles without the negative zero 0x8 (the quantizer
     never writes it)."""

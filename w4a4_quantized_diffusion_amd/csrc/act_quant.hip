@@ -397,20 +397,21 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
         const float inv = 1.0f / den;
         const bool fast = den >= 0x1p-126f && inv < 0x1p126f;
         // as for INT4: the exact division only where the wave needs it
-        float tq[8];
+        uint32_t cq[8];
+        bool nearq[8];
         bool need = !fast;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          tq[j] = (h ? x1[j] : x0[j]) * inv;
-          need |= e2m1_near_mid(tq[j]);
+          cq[j] = e2m1_code_near((h ? x1[j] : x0[j]) * inv, nearq[j]);
+          need |= nearq[j];
         }
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (!fast || e2m1_near_mid(tq[j])) tq[j] = (h ? x1[j] : x0[j]) / den;
+            if (!fast || nearq[j]) cq[j] = e2m1_rne_sat((h ? x1[j] : x0[j]) / den);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w[h] |= e2m1_rne_sat(tq[j]) << (4 * j);
+        for (int j = 0; j < 8; ++j) w[h] |= cq[j] << (4 * j);
       }
     }
     if (ok && live) {

@@ -120,17 +120,34 @@ __device__ __forceinline__ uint32_t e2m1_rne_sat(float t) {
   return (t < 0.f && i != 0) ? (i | 8u) : i;
 }
 
-// rne-to-E2M1 of fl32(z / den) from t = z fl32(1/den): the grid midpoints are
-// exact binary32 values, so only a t within 2^-18 of one can round
-// differently from the correctly rounded quotient; those repeat the exact
-// division.
-__device__ __forceinline__ bool e2m1_near_mid(float t) {
+// E2M1 nibble of t (as e2m1_rne_sat) by arithmetic, and whether t lies so
+// close to a rounding boundary that a t carrying a few ulps of error could
+// round differently (the caller then redoes the quotient exactly).
+//  * |t| < 1: the grid is 0, 0.5, 1 (codes 0..2): code = rne(2|t|); a
+//    boundary is where 2|t| is a half-integer.
+//  * |t| >= 1: E2M1 has one mantissa bit, so rounding the binary32 mantissa
+//    to one bit (ties to even) gives the code directly: the carry moves into
+//    the exponent, code = (exponent field << 1 | mantissa bit) - 252,
+//    saturated at 7 (6.0).  A boundary is where the 22 dropped mantissa bits
+//    are exactly 0x200000; "near" is within 32 units of it, at least 2^-18
+//    absolute for |t| < 8 (well above the error of a reciprocal product).
+// A value rounding to zero gets +0 (code 0, never 0x8).
+__device__ __forceinline__ uint32_t e2m1_code_near(float t, bool& near) {
   const float a = fabsf(t);
-  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.f};
-  bool near = false;
-#pragma unroll
-  for (int i = 0; i < 7; ++i) near |= fabsf(a - mids[i]) <= 0x1p-18f;
-  return near;
+  const float x = a + a;
+  const float rx = rintf(x);
+  const uint32_t csub = uint32_t(rx);
+  const bool nsub = fabsf(x - rx) >= 0.5f - 0x1p-17f;
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = u + 0x1FFFFFu + ((u >> 22) & 1u);
+  uint32_t cn = (r >> 22) - 252u;
+  cn = cn > 7u ? 7u : cn;
+  const uint32_t dropped = u & 0x3FFFFFu;
+  const bool nn = (dropped - (0x200000u - 32u)) <= 64u;
+  const bool small = a < 1.f;
+  const uint32_t c = small ? csub : cn;
+  near = small ? nsub : nn;
+  return (t < 0.f && c != 0u) ? (c | 8u) : c;
 }
 
 // Store one wave's tile of 32x32 f32 MFMA results (RBL x CBL blocks; lane l
