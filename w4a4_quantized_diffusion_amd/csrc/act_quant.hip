@@ -285,7 +285,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
       for (int j = 0; j < 8; ++j) {
         t0[j] = x0[j] * inv;
         t1[j] = x1[j] * inv;
-        need |= near_half(t0[j]) | near_half(t1[j]);
+        need |= unsigned(near_half(t0[j])) | unsigned(near_half(t1[j]));
       }
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll

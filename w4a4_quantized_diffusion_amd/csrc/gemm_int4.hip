@@ -95,10 +95,6 @@ template <int OFF>
 __device__ __forceinline__ void lds_store_b64(uint32_t addr, v2i_t d) {
   asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF));
 }
-template <int OFF>
-__device__ __forceinline__ void lds_store_b128(uint32_t addr, v4i d) {
-  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF));
-}
 __device__ __forceinline__ v2i_t widen8(uint32_t word) {
   uint32_t lo, hi;
   nib8_to_e4m3(word, lo, hi);
@@ -122,23 +118,6 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base) {
   return v8i{int(x.x), int(x.y), int(x.z), int(x.w), int(y.x), int(y.y), int(y.z), int(y.w)};
 }
 
-// Widen 32 packed bytes (64 nibbles) into 64 E4M3 bytes in an LDS row.
-__device__ __forceinline__ void unpack_row(const uint4& p0, const uint4& p1, uint8_t* dst) {
-  uint32_t o[16];
-  nib8_to_e4m3(p0.x, o[0], o[1]);
-  nib8_to_e4m3(p0.y, o[2], o[3]);
-  nib8_to_e4m3(p0.z, o[4], o[5]);
-  nib8_to_e4m3(p0.w, o[6], o[7]);
-  nib8_to_e4m3(p1.x, o[8], o[9]);
-  nib8_to_e4m3(p1.y, o[10], o[11]);
-  nib8_to_e4m3(p1.z, o[12], o[13]);
-  nib8_to_e4m3(p1.w, o[14], o[15]);
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  d[2] = make_uint4(o[8], o[9], o[10], o[11]);
-  d[3] = make_uint4(o[12], o[13], o[14], o[15]);
-}
 
 template <int RK, bool YBF16, bool BBF16>
 __global__ __launch_bounds__(NT) void gemm_int4_kernel(
@@ -154,7 +133,6 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, r32 = lane & 31;
-  const uint32_t hm = h ? 0u : 0xFFFFFFFFu;   // k-slot half 1 carries one piece pair
 
   // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
   // give each XCD a contiguous run of tiles (M fastest) to share its L2.
@@ -164,7 +142,6 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
   const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
   const int G = K / 64;
-  const int64_t KP = K / 2;
 
   // staging role: waves 0..3 stage the 256 A rows of the tile (64 each),
   // waves 4..7 the 256 B rows; thread tid widens row tid % 256 of its side.
