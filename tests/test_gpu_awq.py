@@ -83,7 +83,8 @@ def test_awq_linear_decode_sizes(m):
     _check_linear(m, 3072, 12288, seed=0, ybf16=True)
 
 
-@pytest.mark.parametrize("m,k,n", [(3, 192, 48), (77, 640, 144), (300, 1024, 272)])
+@pytest.mark.parametrize("m,k,n", [(3, 192, 48), (77, 640, 144), (300, 1024, 272),
+                                   (1, 64, 16), (40, 128, 48), (200, 64, 16)])
 def test_awq_linear_ragged(m, k, n):
     _check_linear(m, k, n, seed=2, ybf16=False)
 

@@ -101,8 +101,11 @@ def test_linear_small_workload(ybf16):
 
 
 @pytest.mark.parametrize("m,k,n,rank", [(77, 192, 48, 16), (300, 1024, 272, 32),
-                                        (129, 640, 144, 0), (5, 3072, 400, 48)])
+                                        (129, 640, 144, 0), (5, 3072, 400, 48),
+                                        (1, 64, 16, 0), (300, 64, 272, 32), (33, 128, 48, 16)])
 def test_linear_ragged_shapes(m, k, n, rank):
+    """Ragged M / N tiles; K = 64 and 128 leave most waves of the activation
+    kernel without a K-group and run the GEMM with one or two groups."""
     s = synth.layer(m, k, n, rank, seed=3, workload="attn")
     lay = _oracle_layer(s["w"], s["x"], rank)
     d = layer_to_device(lay, rank, n, k)

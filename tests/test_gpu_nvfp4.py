@@ -156,7 +156,8 @@ def test_nvfp4_linear_small_workload(ybf16):
 
 
 @pytest.mark.parametrize("m,k,n,rank", [(77, 192, 48, 16), (300, 1024, 272, 32),
-                                        (129, 640, 144, 0), (5, 3072, 400, 48)])
+                                        (129, 640, 144, 0), (5, 3072, 400, 48),
+                                        (1, 64, 16, 0), (300, 64, 272, 32)])
 def test_nvfp4_linear_ragged_shapes(m, k, n, rank):
     s = synth.layer(m, k, n, rank, seed=13, workload="mlp_fp4")
     lay = _oracle_layer(s["w"], s["x"], rank)
