@@ -130,3 +130,13 @@ def test_zero_rows_is_a_noop(lib):
                                  None) == 0
     assert lib.awq_linear_w4a16(None, 0, 128, 64, 64, None, None, None, None, None, 1,
                                 None) == 0
+
+
+def test_smoke_inputs_are_contiguous():
+    """Every tensor smoke() hands the binding is contiguous (the binding
+    rejects strided tensors)."""
+    import __graft_entry__ as ge
+    _, _, _, layer = ge.smoke_inputs("cpu")
+    for k, v in layer.items():
+        if hasattr(v, "is_contiguous"):
+            assert v.is_contiguous(), k
