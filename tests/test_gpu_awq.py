@@ -94,3 +94,23 @@ def test_awq_linear_full_size_sampled_rows():
     m = 4608
     rows = np.concatenate([np.random.default_rng(3).choice(m, 16, replace=False), [0, m - 1]])
     _check_linear(m, 3072, 12288, seed=0, rows=rows, ybf16=True)
+
+
+@pytest.mark.parametrize("m", [16, 200])
+def test_awq_linear_deterministic_and_fully_written(m):
+    """Both kernels (M <= 64 and larger M): two runs give the same bits,
+    every element of Y is written and nothing past its end."""
+    k, n = 1024, 336
+    x = synth.activations(m, k, 5, AWQ, 0)
+    w = synth.gaussian((n, k), 0.02, 5, AWQ, 1)
+    q, s, z, _ = OA.quantize_weights(w)
+    lay = awq_layer_to_device(q, s, z, n, k)
+    xt = t_x(x, True)
+    buf = torch.full((m * n + 4096,), float("nan"), dtype=torch.float32, device="cuda")
+    y1 = buf[:m * n].view(m, n)
+    svdq.awq_linear_w4a16(xt, lay, Y=y1)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y1).any(), "unwritten output elements"
+    assert torch.isnan(buf[m * n:]).all(), "write past the end of Y"
+    y2 = svdq.awq_linear_w4a16(xt, lay, y_dtype=torch.float32)
+    assert torch.equal(y1, y2), "two runs differ"

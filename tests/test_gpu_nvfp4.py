@@ -211,3 +211,20 @@ def test_nvfp4_mlp_up_full_size_sampled_rows():
     rows = np.concatenate([rows, [0, m - 1]])
     y_ref, _ = O4.linear_nvfp4(x[rows], lay)
     assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, "MLP-up rows")
+
+
+def test_nvfp4_linear_deterministic_and_fully_written():
+    """Two runs give the same bits; every element of Y is written and
+    nothing past its end (Y inside a NaN-filled buffer)."""
+    s = synth.layer(200, 1024, 336, 32, seed=4, workload="mlp_fp4")
+    lay = _oracle_layer(s["w"], s["x"], 32)
+    d = nv_layer_to_device(lay, 32, 336, 1024)
+    x = t_x(s["x"], True)
+    buf = torch.full((200 * 336 + 4096,), float("nan"), dtype=torch.float32, device="cuda")
+    y1 = buf[:200 * 336].view(200, 336)
+    svdq.svdq_linear_w4a4(x, d, Y=y1)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y1).any(), "unwritten output elements"
+    assert torch.isnan(buf[200 * 336:]).all(), "write past the end of Y"
+    y2 = svdq.svdq_linear_w4a4(x, d)
+    assert torch.equal(y1, y2), "two runs differ"
