@@ -229,21 +229,28 @@ constexpr int STAGE = (BM + BN) * ROWB;
 
 // One staged row's K chunk: an A row's 64 bf16 of X (x0..x7), or a B row's
 // 64 nibbles (x0, x1) with its scale and -zero*scale (x2.x, x2.y).
+// One K chunk of one thread's staging share: half an A row (32 bf16 of X)
+// and half a B row (32 codes with the row's scale and -zero*scale).
 struct Chunk {
-  uint4 x0, x1, x2, x3, x4, x5, x6, x7;
+  uint4 x0, x1, x2, x3;
+  uint4 w;
+  float s, zs;
 };
 
-// 16-byte piece I of the staged A row (I a compile-time constant)
+// 16-byte piece I of the staged A half row (I a compile-time constant)
 template <int I>
 __device__ __forceinline__ uint4 xpiece(const Chunk& c) {
   if constexpr (I == 0) return c.x0;
   else if constexpr (I == 1) return c.x1;
   else if constexpr (I == 2) return c.x2;
-  else if constexpr (I == 3) return c.x3;
-  else if constexpr (I == 4) return c.x4;
-  else if constexpr (I == 5) return c.x5;
-  else if constexpr (I == 6) return c.x6;
-  else return c.x7;
+  else return c.x3;
+}
+template <int I>
+__device__ __forceinline__ uint32_t wword(const Chunk& c) {
+  if constexpr (I == 0) return c.w.x;
+  else if constexpr (I == 1) return c.w.y;
+  else if constexpr (I == 2) return c.w.z;
+  else return c.w.w;
 }
 
 __global__ __launch_bounds__(NT) void awq_gemm_kernel(
@@ -265,47 +272,31 @@ __global__ __launch_bounds__(NT) void awq_gemm_kernel(
   const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
   const int G = K / 64;
 
-  // staging: waves 0..3 stage the 256 A rows (X), waves 4..7 the 256 B rows
-  // (weights); thread tid owns staged row tid.  Rows past the edge repeat the
-  // last row (their products only reach outputs that are never stored).
-  const bool is_a = wave < 4;
-  const int64_t ra = m0 + (tid & 255) < M ? m0 + (tid & 255) : M - 1;
-  const int64_t rb = n0 + (tid & 255) < N ? n0 + (tid & 255) : N - 1;
+  // staging: thread tid stages half of A row tid / 2 (X) and half of B row
+  // tid / 2 (weights), the half tid % 2 of the chunk's 64 k, so every
+  // thread copies 64 bytes and dequantizes 32 codes per chunk.  Rows past
+  // the edge repeat the last row (their products only reach outputs that
+  // are never stored).
+  const int srow = tid >> 1, half = tid & 1;
+  const int64_t ra = m0 + srow < M ? m0 + srow : M - 1;
+  const int64_t rb = n0 + srow < N ? n0 + srow : N - 1;
   auto load_chunk = [&](int g, Chunk& ch) {
-    if (is_a) {
-      const uint4* xp = reinterpret_cast<const uint4*>(X + ra * K + 64 * g);
-      ch.x0 = xp[0];
-      ch.x1 = xp[1];
-      ch.x2 = xp[2];
-      ch.x3 = xp[3];
-      ch.x4 = xp[4];
-      ch.x5 = xp[5];
-      ch.x6 = xp[6];
-      ch.x7 = xp[7];
-    } else {
-      const uint4* wp = reinterpret_cast<const uint4*>(q + (int64_t(g) * N + rb) * 32);
-      ch.x0 = wp[0];
-      ch.x1 = wp[1];
-      const float s = bf16_to_f32(sc[int64_t(g) * N + rb]);
-      const float zs = -bf16_to_f32(zr[int64_t(g) * N + rb]) * s;
-      ch.x2 = make_uint4(__float_as_uint(s), __float_as_uint(zs), 0, 0);
-    }
+    const uint4* xp = reinterpret_cast<const uint4*>(X + ra * K + 64 * g + 32 * half);
+    ch.x0 = xp[0];
+    ch.x1 = xp[1];
+    ch.x2 = xp[2];
+    ch.x3 = xp[3];
+    ch.w = *reinterpret_cast<const uint4*>(q + (int64_t(g) * N + rb) * 32 + 16 * half);
+    ch.s = bf16_to_f32(sc[int64_t(g) * N + rb]);
+    ch.zs = -bf16_to_f32(zr[int64_t(g) * N + rb]) * ch.s;
   };
-  // quarter P (k 16P .. 16P+15) of a staged chunk into LDS; P is a
-  // compile-time constant so the chunk stays in registers
+  // quarter P of a thread's share (A piece P, B word P: k 32 half + 8P ..)
+  // into LDS; P is a compile-time constant so the chunk stays in registers
   auto stage_quarter = [&](uint8_t* st, const Chunk& ch, auto PC) {
     constexpr int P = decltype(PC)::value;
-    uint4* d = reinterpret_cast<uint4*>(st + tid * ROWB + P * 32);
-    if (is_a) {
-      d[0] = xpiece<2 * P>(ch);
-      d[1] = xpiece<2 * P + 1>(ch);
-    } else {
-      const uint32_t w0 = P == 0 ? ch.x0.x : P == 1 ? ch.x0.z : P == 2 ? ch.x1.x : ch.x1.z;
-      const uint32_t w1 = P == 0 ? ch.x0.y : P == 1 ? ch.x0.w : P == 2 ? ch.x1.y : ch.x1.w;
-      const float s = __uint_as_float(ch.x2.x), zs = __uint_as_float(ch.x2.y);
-      d[0] = dequant8(w0, s, zs);
-      d[1] = dequant8(w1, s, zs);
-    }
+    *reinterpret_cast<uint4*>(st + srow * ROWB + half * 64 + P * 16) = xpiece<P>(ch);
+    *reinterpret_cast<uint4*>(st + (BM + srow) * ROWB + half * 64 + P * 16) =
+        dequant8(wword<P>(ch), ch.s, ch.zs);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
