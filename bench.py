@@ -37,8 +37,8 @@ PEAK_FP4_TFLOPS = 10100.0       # dense fp4 / fp6 MFMA
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--nbuf", type=int, default=4, help="distinct X / Y buffers rotated")
@@ -266,20 +266,12 @@ def main():
         svdq.svdq_linear_w4a4(xs[i % args.nbuf], layer, bias, workspace=ws,
                               Y=ys[i % args.nbuf])
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # eager: one library call per step from Python
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
-
-    # the same steps captured into HIP graphs (one per X / Y buffer) and
-    # replayed: the two kernels per step without host launch gaps
+    # The timed steps replay HIP graphs of the library calls, as a model's
+    # forward pass would: one graph holds nbuf consecutive layer calls (each
+    # on its own X / Y buffer), smaller ones the remainders of W and K modulo
+    # nbuf, so exactly W and K steps run.  Warmup replays come right before the timed ones:
+    # the GPU lowers its clock after a few ms idle and takes some tens of ms
+    # of load to raise it again.
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -287,23 +279,44 @@ def main():
             step(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for i in range(args.nbuf):
+
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(i)
-        graphs.append(g)
-    for i in range(args.nbuf):
-        graphs[i].replay()
+            for i in range(n):
+                step(i)
+        return g
+
+    graphs = {n: capture(n) for n in {args.nbuf, args.steps % args.nbuf, args.warmup % args.nbuf}
+              if n}
+
+    def run_steps(k):
+        for _ in range(k // args.nbuf):
+            graphs[args.nbuf].replay()
+        if k % args.nbuf:
+            graphs[k % args.nbuf].replay()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
-    for i in range(args.steps):
-        graphs[i % args.nbuf].replay()
+    run_steps(args.steps)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
+
+    # eager: one library call per step from Python, for reference
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
 
     # per-kernel durations, HIP events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -347,7 +360,8 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / PEAK_FP8_TOPS, 2),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
         "eager_ms_per_step": round(ms_eager, 5),
-        "timing": "HIP graph of the layer's steps replayed (eager per-call loop in eager_ms_per_step)",
+        "timing": f"HIP graphs of {args.nbuf} consecutive layer calls replayed after the warmup "
+                  "replays (eager per-call loop in eager_ms_per_step)",
         "roofline": {
             "kernel": "gemm_int4_kernel",
             "bound": "mfma",

@@ -239,3 +239,43 @@ def test_linear_graph_replay_matches_eager():
         assert torch.equal(y, y_eager), f"replay {rep} differs from the eager call"
         svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, y_dtype=torch.bfloat16)   # eager in between
         torch.cuda.synchronize()
+
+
+def test_linear_graph_of_consecutive_calls():
+    """Three layer calls on different X / Y buffers sharing one workspace,
+    captured into one HIP graph (the benchmark replays such a graph): every
+    replay gives each call's eager output bit for bit, so the calls inside the
+    graph stay ordered on the workspace."""
+    s = synth.layer(300, 1024, 272, 32, seed=10, workload="attn")
+    lay = _oracle_layer(s["w"], s["x"], 32)
+    d = layer_to_device(lay, 32, 272, 1024)
+    xs = [t_x(s["x"], True)] + [
+        t_x(synth.activations(300, 1024, 0, synth.WORKLOADS["attn"], 20 + i), True)
+        for i in range(2)]
+    bias = torch.from_numpy(s["b"]).to("cuda").to(torch.bfloat16)
+    ws = torch.empty(svdq.svdq_workspace_bytes(300, 1024, 32), dtype=torch.uint8, device="cuda")
+    eager = [svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, y_dtype=torch.bfloat16) for x in xs]
+    torch.cuda.synchronize()
+    assert not torch.equal(eager[0], eager[1])
+    ys = [torch.empty_like(e) for e in eager]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for x, y in zip(xs, ys):
+            svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, Y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, y in zip(xs, ys):
+            svdq.svdq_linear_w4a4(x, d, bias, workspace=ws, Y=y)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (y, e) in enumerate(zip(ys, eager)):
+            assert torch.equal(y, e), f"replay {rep}, call {i} differs from the eager call"
+        svdq.svdq_linear_w4a4(xs[1], d, bias, workspace=ws, y_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
