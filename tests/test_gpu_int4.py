@@ -51,6 +51,31 @@ def test_act_quant_bf16_ragged_rows(m):
     _check_act(s["x"], lay, 32, bf16=True)
 
 
+def test_act_quant_half_integer_ties():
+    """Group amax 14 (scale 2, exact reciprocal) and 21 (scale 3, inexact
+    reciprocal): every quotient that is a half-integer 0.5 ... 6.5, the values
+    one ulp on either side of it, both signs, so that each tie and each
+    near-tie is decided by the correctly rounded quotient (the reciprocal
+    alone would misjudge some for scale 3).  Codes and scales must match the
+    oracle bit for bit; -0.5 and the values just above it give code 0."""
+    k, m = 512, 16
+    halves = np.arange(7, dtype=np.float32) + np.float32(0.5)
+    x = np.zeros((m, k), np.float32)
+    for r in range(m):
+        for g in range(k // 64):
+            s = np.float32(2.0 if (r + g) % 2 else 3.0)
+            z = halves * s
+            vals = np.concatenate([z, np.nextafter(z, np.float32(0)), np.nextafter(z, np.float32(99))])
+            vals = np.concatenate([vals, -vals])
+            x[r, 64 * g] = 7 * s if (r + g) % 3 else -7 * s
+            for i in range(1, 64):
+                x[r, 64 * g + i] = vals[(r * 5 + g * 11 + i) % vals.size]
+    lay = dict(smooth=np.ones(k, np.float32), q=np.zeros((16, k), np.int8),
+               wcodes=np.zeros((16, k // 2), np.uint8), sW=np.ones((16, k // 64), np.float32),
+               lora_down=None, lora_up=None)
+    _check_act(x, lay, 0, bf16=False)
+
+
 def test_gemm_unit_scale_exact_integers():
     """rank 0, all scales 1, no bias, fp32 out: Y is the exact integer dot
     product of the codes (below 2^24, so exact in fp32)."""

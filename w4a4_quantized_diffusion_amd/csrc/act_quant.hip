@@ -43,24 +43,40 @@ struct XRaw {
   uint4 v[XF32 ? 4 : 2];
 };
 
-// lora_down fragments of one lane for one K group (both 8-wide chunks, all
-// 16-row blocks of the rank), prefetched with X when the rank is small
+// lora_down of one K group (all 16 R rank rows, 64 columns), prefetched with
+// X when the rank is small.  The MFMA wants 8 consecutive k of one rank row
+// per lane with the rank across lanes, so a direct load touches one cache line
+// per lane; instead lane l loads the 16 bytes at rank (l / 8) + 8 i, column
+// chunk l % 8 (eight lanes cover one rank's 128 contiguous bytes), and the
+// wave passes them through a private LDS tile into the MFMA layout.
 constexpr int RB_PREFETCH = 2;
 template <int RB>
 struct DownRaw {
   uint4 v[RB > 0 && RB <= RB_PREFETCH ? 2 * RB : 1];
 };
+// the tile: rank rows of 8 chunks of 16 bytes, padded to 144 bytes so that
+// the 16 lanes of an MFMA operand read (16 ranks, one chunk) hit distinct banks
+constexpr int DOWN_ROW = 144;
 
 template <int RB>
-__device__ __forceinline__ void load_down(const uint16_t* __restrict__ down, int K, int r, int k0,
-                                          DownRaw<RB>& d) {
+__device__ __forceinline__ void load_down(const uint16_t* __restrict__ down, int K, int lane,
+                                          int kg, DownRaw<RB>& d) {
   if constexpr (RB > 0 && RB <= RB_PREFETCH) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const uint16_t* p = down + int64_t(rb * 16 + r) * K + k0;
-      d.v[2 * rb] = *reinterpret_cast<const uint4*>(p);
-      d.v[2 * rb + 1] = *reinterpret_cast<const uint4*>(p + 32);
+    for (int i = 0; i < 2 * RB; ++i) {
+      const uint16_t* p = down + int64_t((lane >> 3) + 8 * i) * K + kg + 8 * (lane & 7);
+      d.v[i] = *reinterpret_cast<const uint4*>(p);
     }
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void stage_down(uint8_t* tile, int lane, const DownRaw<RB>& d) {
+  if constexpr (RB > 0 && RB <= RB_PREFETCH) {
+#pragma unroll
+    for (int i = 0; i < 2 * RB; ++i)
+      *reinterpret_cast<v4i*>(tile + ((lane >> 3) + 8 * i) * DOWN_ROW + (lane & 7) * 16) =
+          v4i{int(d.v[i].x), int(d.v[i].y), int(d.v[i].z), int(d.v[i].w)};
   }
 }
 
@@ -141,16 +157,31 @@ __device__ __forceinline__ void unpack_smooth(const SmoothRaw& r, float (&s0)[8]
 
 // t = z fl32(1/s) lies within 2^-20 of fl32(z / s) for |z| <= 7 s; only a
 // t within 2^-19 of a half-integer can round differently from the quotient.
-__device__ __forceinline__ bool near_half(float t) {
-  const float fr = fabsf(t - truncf(t));
-  return fabsf(fr - 0.5f) <= 0x1p-19f;
+// Given r = rne(|t|), |t| is that close to a half-integer exactly when it
+// lies at least 1/2 - 2^-19 from r (the difference is exact).
+__device__ __forceinline__ bool near_half_r(float t, float r) {
+  return fabsf(r - fabsf(t)) >= 0.5f - 0x1p-19f;
 }
 
-// sign-magnitude nibble of an integer-valued float in [-7, 7]
-__device__ __forceinline__ uint32_t int4_nibble(float q) {
-  int qi = int(q);
-  qi = qi < -8 ? -8 : (qi > 7 ? 7 : qi);
-  return qi < 0 ? uint32_t(8 | (-qi)) : uint32_t(qi);
+// Sign-magnitude INT4 code of t (|t| < 7.5) as a float, given r = rne(|t|):
+// r + 8 when t < -1/2 (a negative value with a nonzero magnitude).  The
+// clamped fma is 2^24 (-t - 1/2) limited to [0, 1]: 1 for any t below -1/2
+// (the binary32 spacing there is at least 2^-24), 0 otherwise.
+__device__ __forceinline__ float int4_code(float t, float r) {
+  const float neg = __builtin_amdgcn_fmed3f(fmaf(t, -0x1p24f, -0x1p23f), 0.0f, 1.0f);
+  return fmaf(neg, 8.0f, r);
+}
+
+// eight codes (value j in nibble j: the even values in the low nibbles) into
+// one word; each code goes into a byte with v_cvt_pk_u8_f32
+__device__ __forceinline__ uint32_t int4_word(const float (&t)[8], const float (&r)[8]) {
+  uint32_t e = 0, o = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    e = __builtin_amdgcn_cvt_pk_u8_f32(int4_code(t[2 * b], r[2 * b]), b, e);
+    o = __builtin_amdgcn_cvt_pk_u8_f32(int4_code(t[2 * b + 1], r[2 * b + 1]), b, o);
+  }
+  return e | (o << 4);
 }
 
 template <int RB>
@@ -170,17 +201,18 @@ __device__ __forceinline__ void lr_mfma(v4f (&acc)[RB > 0 ? RB : 1], const uint3
   }
 }
 
-// lr_mfma with the lora_down fragments already in registers (half h: the
+// lr_mfma with the group's lora_down in the wave's LDS tile (half h: the
 // chunk at k0 or at k0 + 32)
 template <int RB>
 __device__ __forceinline__ void lr_mfma_pre(v4f (&acc)[RB > 0 ? RB : 1], const uint32_t (&xb)[4],
-                                            const DownRaw<RB>& d, int h) {
+                                            const uint8_t* tile, int lane, int h) {
   if constexpr (RB > 0 && RB <= RB_PREFETCH) {
     v4i ai = {int(xb[0]), int(xb[1]), int(xb[2]), int(xb[3])};
     v8bf a = __builtin_bit_cast(v8bf, ai);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const uint4 bu = d.v[2 * rb + h];
+      const uint4 bu = *reinterpret_cast<const uint4*>(
+          tile + (rb * 16 + (lane & 15)) * DOWN_ROW + ((lane >> 4) + 4 * h) * 16);
       v4i bi = {int(bu.x), int(bu.y), int(bu.z), int(bu.w)};
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, bi),
                                                          acc[rb], 0, 0, 0);
@@ -224,6 +256,8 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
   const int64_t row = row0 + r;
   const bool ok = row < M;
   const int G = K / 64;
+  uint8_t* const dtile = reinterpret_cast<uint8_t*>(red + WAVES * ROWS * RB * 16) +
+                         wave * (RB * 16 * DOWN_ROW);
   v4f acc[RB > 0 ? RB : 1];
 #pragma unroll
   for (int i = 0; i < (RB > 0 ? RB : 1); ++i) acc[i] = v4f{0, 0, 0, 0};
@@ -244,7 +278,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     const int gg = tc >= 0 ? wave + WAVES * tc : 0;
     load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
     load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
-    load_down<RB>(down, K, r, gg * 64 + 8 * q, dring[sl_]);
+    load_down<RB>(down, K, lane, gg * 64, dring[sl_]);
   };
 #pragma unroll
   for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
@@ -279,26 +313,31 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
       // quotients through the reciprocal; only when some lane of the wave
       // has one within 2^-19 of a half-integer (or a tiny scale) does the
       // wave take the exact divisions, for those values
-      float t0[8], t1[8];
+      float t0[8], t1[8], r0[8], r1[8];
       bool need = !fast;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         t0[j] = x0[j] * inv;
         t1[j] = x1[j] * inv;
-        need |= unsigned(near_half(t0[j])) | unsigned(near_half(t1[j]));
+        r0[j] = rintf(fabsf(t0[j]));
+        r1[j] = rintf(fabsf(t1[j]));
+        need |= unsigned(near_half_r(t0[j], r0[j])) | unsigned(near_half_r(t1[j], r1[j]));
       }
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          if (!fast || near_half(t0[j])) t0[j] = x0[j] / s;
-          if (!fast || near_half(t1[j])) t1[j] = x1[j] / s;
+          if (!fast || near_half_r(t0[j], r0[j])) {
+            t0[j] = x0[j] / s;
+            r0[j] = rintf(fabsf(t0[j]));
+          }
+          if (!fast || near_half_r(t1[j], r1[j])) {
+            t1[j] = x1[j] / s;
+            r1[j] = rintf(fabsf(t1[j]));
+          }
         }
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        w0 |= int4_nibble(rintf(t0[j])) << (4 * j);
-        w1 |= int4_nibble(rintf(t1[j])) << (4 * j);
-      }
+      w0 = int4_word(t0, r0);
+      w1 = int4_word(t1, r1);
     }
     if (ok && live) {
       // group-major layout: the 32 bytes of (group g, row) follow those of
@@ -309,8 +348,9 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
       if (q == 0) scales[int64_t(g) * M + row] = s;
     }
     if constexpr (RB <= RB_PREFETCH) {
-      lr_mfma_pre<RB>(acc, b0, dring[sl], 0);
-      lr_mfma_pre<RB>(acc, b1, dring[sl], 1);
+      stage_down<RB>(dtile, lane, dring[sl]);
+      lr_mfma_pre<RB>(acc, b0, dtile, lane, 0);
+      lr_mfma_pre<RB>(acc, b1, dtile, lane, 1);
     } else {
       lr_mfma<RB>(acc, b0, down, K, r, k0);
       lr_mfma<RB>(acc, b1, down, K, r, k1);
@@ -339,6 +379,8 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
   const int G = K / 64;            // 64-wide steps: 4 NVFP4 blocks each
   const float ts = *ts_x;
   const float d = 6.0f * ts;
+  uint8_t* const dtile = reinterpret_cast<uint8_t*>(red + WAVES * ROWS * RB * 16) +
+                         wave * (RB * 16 * DOWN_ROW);
   v4f acc[RB > 0 ? RB : 1];
 #pragma unroll
   for (int i = 0; i < (RB > 0 ? RB : 1); ++i) acc[i] = v4f{0, 0, 0, 0};
@@ -357,7 +399,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
     const int gg = tc >= 0 ? wave + WAVES * tc : 0;
     load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
     load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
-    load_down<RB>(down, K, r, gg * 64 + 8 * q, dring[sl_]);
+    load_down<RB>(down, K, lane, gg * 64, dring[sl_]);
   };
 #pragma unroll
   for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
@@ -427,8 +469,9 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
       }
     }
     if constexpr (RB <= RB_PREFETCH) {
-      lr_mfma_pre<RB>(acc, b0, dring[sl], 0);
-      lr_mfma_pre<RB>(acc, b1, dring[sl], 1);
+      stage_down<RB>(dtile, lane, dring[sl]);
+      lr_mfma_pre<RB>(acc, b0, dtile, lane, 0);
+      lr_mfma_pre<RB>(acc, b1, dtile, lane, 1);
     } else {
       lr_mfma<RB>(acc, b0, down, K, r, k0);
       lr_mfma<RB>(acc, b1, down, K, r, k1);
@@ -450,12 +493,19 @@ struct RankDispatch {
   }
 };
 
+// LR reduction buffer, then (small ranks) the waves' lora_down tiles
+constexpr size_t lds_bytes(int RB) {
+  return RB > 0 ? size_t(WAVES) * ROWS * RB * 16 * sizeof(float) +
+                      (RB <= RB_PREFETCH ? size_t(WAVES) * RB * 16 * DOWN_ROW : 0)
+                : 0;
+}
+
 template <int RB, bool XF32>
 struct Int4Launch {
   static svdq_status go(const void* X, int M, int K, const float* smooth,
                         const uint16_t* down, uint8_t* codes, float* scales, uint16_t* LR,
                         hipStream_t s) {
-    const size_t shm = RB > 0 ? size_t(WAVES) * ROWS * RB * 16 * sizeof(float) : 0;
+    const size_t shm = lds_bytes(RB);
     if (shm > 65536 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_int4_kernel<RB, XF32>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
@@ -472,7 +522,7 @@ struct Fp4Launch {
   static svdq_status go(const void* X, int M, int K, const float* smooth,
                         const uint16_t* down, const float* ts_x, uint8_t* codes,
                         uint8_t* scales, uint16_t* LR, hipStream_t s) {
-    const size_t shm = RB > 0 ? size_t(WAVES) * ROWS * RB * 16 * sizeof(float) : 0;
+    const size_t shm = lds_bytes(RB);
     if (shm > 65536 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_nvfp4_kernel<RB, XF32>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
