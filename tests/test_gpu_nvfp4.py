@@ -95,6 +95,32 @@ def test_nvfp4_act_quant_grid_midpoints():
     _check_act(x, lay, 0, bf16=False)
 
 
+def test_nvfp4_act_quant_block_scale_ties():
+    """Tensor scale 1 (divisor 6): block amaxes whose quotient a / 6 is an
+    E4M3 grid point, a midpoint between two (normal and subnormal range), one
+    ulp on either side of it, and values past 448 that saturate.  The block
+    scales and the codes they lead to must match the oracle bit for bit."""
+    vals = F.E4M3_POS[1:]
+    mids = (vals[1:] + vals[:-1]) / 2
+    a = (np.concatenate([vals, mids]) * 6).astype(np.float32)
+    a = a[(a > 0) & np.isfinite(a)]
+    amax = np.concatenate([a, np.nextafter(a, np.float32(0)), np.nextafter(a, np.float32(1e9)),
+                           np.array([2700, 2784, 2800, 1e5], np.float32)])
+    k = 256
+    m = -(-amax.size // (k // 16))
+    x = np.zeros((m, k), np.float32)
+    g = np.random.default_rng(5)
+    for i, v in enumerate(amax):
+        r, b_ = divmod(i, k // 16)
+        blk = g.uniform(-1, 1, 16).astype(np.float32) * v
+        blk[(i * 7) % 16] = v if i % 2 else -v
+        x[r, 16 * b_:16 * b_ + 16] = blk
+    lay = dict(smooth=np.ones(k, np.float32), ts_x=np.float32(1.0), ts_w=np.float32(1.0),
+               codes=np.zeros((16, k), np.uint8), sbw=np.zeros((16, k // 16), np.uint8),
+               lora_down=None, lora_up=None)
+    _check_act(x, lay, 0, bf16=False)
+
+
 def _random_e2m1(g, shape):
     """Random E2M1 nibbles without the negative zero 0x8 (the quantizer
     never writes it)."""

@@ -184,6 +184,54 @@ __device__ __forceinline__ uint32_t int4_word(const float (&t)[8], const float (
   return e | (o << 4);
 }
 
+// NVFP4 by the hardware conversions (v_cvt_scalef32_pk_fp4_f32 rounds to the
+// nearest E2M1 value, ties to even, saturating at 6; v_cvt_scalef32_pk_fp8_f32
+// rounds to the nearest E4M3 value and is given at most 448; both checked
+// against the formats' definitions on the device).  Each quotient is
+// converted twice, from a reciprocal scaled by 1 + 2^-17 and by 1 - 2^-17: the
+// true quotient lies between the two, so when both give the same code it is
+// that code; otherwise the caller repeats the exact division.
+constexpr float PERT_HI = 1.0f + 0x1p-17f, PERT_LO = 1.0f - 0x1p-17f;
+
+// E2M1 code pairs of eight values x_j * inv: byte b of `even` holds the codes
+// of x_{2b} (low nibble: scaled up, high: scaled down), `odd` those of x_{2b+1}
+template <int B>
+__device__ __forceinline__ void e2m1_pair_byte(const float (&x)[8], float inv_hi, float inv_lo,
+                                               uint32_t& even, uint32_t& odd) {
+  even = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(even, x[2 * B] * inv_hi, x[2 * B] * inv_lo,
+                                                  1.0f, B);
+  odd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(odd, x[2 * B + 1] * inv_hi,
+                                                 x[2 * B + 1] * inv_lo, 1.0f, B);
+}
+__device__ __forceinline__ void e2m1_pairs(const float (&x)[8], float inv_hi, float inv_lo,
+                                           uint32_t& even, uint32_t& odd) {
+  even = 0;
+  odd = 0;
+  e2m1_pair_byte<0>(x, inv_hi, inv_lo, even, odd);
+  e2m1_pair_byte<1>(x, inv_hi, inv_lo, even, odd);
+  e2m1_pair_byte<2>(x, inv_hi, inv_lo, even, odd);
+  e2m1_pair_byte<3>(x, inv_hi, inv_lo, even, odd);
+}
+
+// a negative value that rounds to zero comes out of the conversion as 0x8:
+// make those nibbles +0
+__device__ __forceinline__ uint32_t e2m1_clear_negzero(uint32_t w) {
+  const uint32_t low = (w << 1) | (w << 2) | (w << 3);   // bits 0..2 of a nibble, at bit 3
+  return w ^ (w & ~low & 0x88888888u);
+}
+
+// E4M3 block scale code of v = a / d, given a * rcp(d) scaled up and down;
+// the exact quotient only when the two disagree (or d is out of range)
+__device__ __forceinline__ uint32_t e4m3_block_scale(float a, float d, float rd_hi, float rd_lo,
+                                                     bool d_ok) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2s z = {0, 0};
+  const v2s p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(a * rd_hi, 448.0f),
+                                                         fminf(a * rd_lo, 448.0f), 1.0f, false);
+  const uint32_t c0 = uint32_t(p[0]) & 0xFFu, c1 = uint32_t(p[0]) >> 8 & 0xFFu;
+  return (c0 == c1 && d_ok) ? c0 : e4m3_rne_sat(a / d);
+}
+
 template <int RB>
 __device__ __forceinline__ void lr_mfma(v4f (&acc)[RB > 0 ? RB : 1], const uint32_t (&xb)[4],
                                         const uint16_t* __restrict__ down, int K, int r,
@@ -379,6 +427,9 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
   const int G = K / 64;            // 64-wide steps: 4 NVFP4 blocks each
   const float ts = *ts_x;
   const float d = 6.0f * ts;
+  const float rd = __builtin_amdgcn_rcpf(d);
+  const float rd_hi = rd * PERT_HI, rd_lo = rd * PERT_LO;
+  const bool d_ok = d >= 0x1p-126f && rd < 0x1p126f;
   uint8_t* const dtile = reinterpret_cast<uint8_t*>(red + WAVES * ROWS * RB * 16) +
                          wave * (RB * 16 * DOWN_ROW);
   v4f acc[RB > 0 ? RB : 1];
@@ -433,27 +484,29 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float a = h ? a1 : a0;
-      sb[h] = e4m3_rne_sat(a / d);
-      const float den = e4m3_value(sb[h]) * ts;
+      const float (&xh)[8] = h ? x1 : x0;
+      sb[h] = e4m3_block_scale(a, d, rd_hi, rd_lo, d_ok);
+      const float den = __builtin_amdgcn_cvt_f32_fp8(int(sb[h]), 0) * ts;
       if (den > 0.f) {
-        const float inv = 1.0f / den;
+        const float inv = __builtin_amdgcn_rcpf(den);
         const bool fast = den >= 0x1p-126f && inv < 0x1p126f;
+        uint32_t ev, od;
+        e2m1_pairs(xh, inv * PERT_HI, inv * PERT_LO, ev, od);
+        const uint32_t differ = ((ev ^ (ev >> 4)) | (od ^ (od >> 4))) & 0x0F0F0F0Fu;
+        uint32_t word = (ev & 0x0F0F0F0Fu) | ((od & 0x0F0F0F0Fu) << 4);
         // as for INT4: the exact division only where the wave needs it
-        uint32_t cq[8];
-        bool nearq[8];
-        bool need = !fast;
+        if (__builtin_amdgcn_ballot_w64(differ != 0 || !fast) != 0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          cq[j] = e2m1_code_near((h ? x1[j] : x0[j]) * inv, nearq[j]);
-          need |= nearq[j];
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t src = (j & 1) ? od : ev;
+            const uint32_t byte = src >> (8 * (j >> 1));
+            if (!fast || ((byte ^ (byte >> 4)) & 15u) != 0) {
+              const uint32_t c = e2m1_rne_sat(xh[j] / den);
+              word = (word & ~(15u << (4 * j))) | (c << (4 * j));
+            }
+          }
         }
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (!fast || nearq[j]) cq[j] = e2m1_rne_sat((h ? x1[j] : x0[j]) / den);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w[h] |= cq[j] << (4 * j);
+        w[h] = e2m1_clear_negzero(word);
       }
     }
     if (ok && live) {

@@ -120,36 +120,6 @@ __device__ __forceinline__ uint32_t e2m1_rne_sat(float t) {
   return (t < 0.f && i != 0) ? (i | 8u) : i;
 }
 
-// E2M1 nibble of t (as e2m1_rne_sat) by arithmetic, and whether t lies so
-// close to a rounding boundary that a t carrying a few ulps of error could
-// round differently (the caller then redoes the quotient exactly).
-//  * |t| < 1: the grid is 0, 0.5, 1 (codes 0..2): code = rne(2|t|); a
-//    boundary is where 2|t| is a half-integer.
-//  * |t| >= 1: E2M1 has one mantissa bit, so rounding the binary32 mantissa
-//    to one bit (ties to even) gives the code directly: the carry moves into
-//    the exponent, code = (exponent field << 1 | mantissa bit) - 252,
-//    saturated at 7 (6.0).  A boundary is where the 22 dropped mantissa bits
-//    are exactly 0x200000; "near" is within 32 units of it, at least 2^-18
-//    absolute for |t| < 8 (well above the error of a reciprocal product).
-// A value rounding to zero gets +0 (code 0, never 0x8).
-__device__ __forceinline__ uint32_t e2m1_code_near(float t, bool& near) {
-  const float a = fabsf(t);
-  const float x = a + a;
-  const float rx = rintf(x);
-  const uint32_t csub = uint32_t(rx);
-  const bool nsub = fabsf(x - rx) >= 0.5f - 0x1p-17f;
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t r = u + 0x1FFFFFu + ((u >> 22) & 1u);
-  uint32_t cn = (r >> 22) - 252u;
-  cn = cn > 7u ? 7u : cn;
-  const uint32_t dropped = u & 0x3FFFFFu;
-  const bool nn = (dropped - (0x200000u - 32u)) <= 64u;
-  const bool small = a < 1.f;
-  const uint32_t c = small ? csub : cn;
-  near = small ? nsub : nn;
-  return (t < 0.f && c != 0u) ? (c | 8u) : c;
-}
-
 // Store one wave's tile of 32x32 f32 MFMA results (RBL x CBL blocks; lane l
 // holds column l%32, rows 8(e/4) + 4(l/32) + e%4 of each block) plus a
 // per-column bias.  One 32-row block row at a time passes through the
