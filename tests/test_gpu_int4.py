@@ -234,6 +234,31 @@ def test_flagship_full_size_sampled_rows():
     assert_lr_close(lr[torch.from_numpy(rows).cuda()], x[rows], lay["lora_down"], "flagship LR")
 
 
+@pytest.mark.parametrize("m,k,n,workload", [(4608, 3072, 9216, "attn"), (4608, 3072, 3072, "attn"),
+                                            (4608, 12288, 3072, "mlp"), (9216, 3072, 12288, "mlp")])
+def test_dit_shapes_full_size_sampled_rows(m, k, n, workload):
+    """The DiT projection shapes at rank 32: attention QKV and output
+    projections at 4608 tokens, the MLP down-projection (K 12288), the MLP
+    up-projection at batch 2 (M 9216).  Activation codes / scales bit-exact on
+    every row, Y and LR on sampled rows (first and last included)."""
+    rank = 32
+    x = synth.layer(m, k, 16, 0, seed=2, workload=workload)["x"]
+    lay = random_int4_layer(n, k, rank, seed=2, workload=workload)
+    d = layer_to_device(lay, rank, n, k)
+    ws = torch.empty(svdq.svdq_workspace_bytes(m, k, rank), dtype=torch.uint8, device="cuda")
+    y = svdq.svdq_linear_w4a4(t_x(x, True), d, workspace=ws, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    codes, scales, lr = svdq.workspace_views(ws, m, k, rank)
+    qx, sa = O.quantize_activations(x, lay["smooth"])
+    assert np.array_equal(rm_codes(codes.cpu().numpy()), O.pack_int4(qx))
+    assert np.array_equal(scales.cpu().numpy().T, sa)
+    rows = np.random.default_rng(1).choice(m, 16, replace=False)
+    rows = np.concatenate([rows, [0, m - 1]])
+    y_ref, _ = O.linear_w4a4(x[rows], lay)
+    assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, f"{workload} M{m} K{k} N{n} rows")
+    assert_lr_close(lr[torch.from_numpy(rows).cuda()], x[rows], lay["lora_down"], "LR")
+
+
 def test_linear_graph_replay_matches_eager():
     """The layer captured into a HIP graph (the benchmark replays one): every
     replay, with eager work and synchronisations in between, gives the eager

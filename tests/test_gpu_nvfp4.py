@@ -211,10 +211,12 @@ def test_nvfp4_quantize_weights_given_lowrank_bit_exact():
     assert np.array_equal(rm_scales(out["wscales"].cpu().numpy()), lay["sbw"]), "scales differ"
 
 
-def test_nvfp4_mlp_up_full_size_sampled_rows():
-    """M 4608, K 3072, N 12288, rank 32 (the MLP up-projection shape):
-    activation codes / scales bit-exact on every row, Y on sampled rows."""
-    m, k, n, rank = 4608, 3072, 12288, 32
+@pytest.mark.parametrize("m,k,n", [(4608, 3072, 12288), (4608, 12288, 3072), (9216, 3072, 12288)])
+def test_nvfp4_mlp_up_full_size_sampled_rows(m, k, n):
+    """The MLP pair at rank 32: up-projection (K 3072 -> N 12288) at 4608
+    tokens and at batch 2 (M 9216), down-projection (K 12288 -> N 3072).
+    Activation codes / scales bit-exact on every row, Y on sampled rows."""
+    rank = 32
     x = synth.layer(m, k, 16, 0, seed=0, workload="mlp_fp4")["x"]
     base = random_int4_layer(n, k, rank, seed=0, workload="mlp_fp4")
     g = np.random.default_rng(23)
@@ -236,7 +238,7 @@ def test_nvfp4_mlp_up_full_size_sampled_rows():
     rows = np.random.default_rng(1).choice(m, 16, replace=False)
     rows = np.concatenate([rows, [0, m - 1]])
     y_ref, _ = O4.linear_nvfp4(x[rows], lay)
-    assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, "MLP-up rows")
+    assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, f"MLP M{m} K{k} N{n} rows")
 
 
 def test_nvfp4_linear_deterministic_and_fully_written():
