@@ -126,6 +126,8 @@ __device__ __forceinline__ uint32_t e2m1_rne_sat(float t) {
 // wave's private LDS buffer `eb` (32 x (32 CBL + 4) floats), so that every
 // lane writes whole 16-byte pieces of output rows instead of 2- or 4-byte
 // scattered elements.  The caller makes `eb` free (no other wave uses it).
+// The output is written once and not read again by the kernel, so the
+// stores are non-temporal (measured 1-2% faster for the GEMMs' Y).
 template <int RBL, int CBL, bool YBF16>
 __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[RBL][CBL],
                                                 const float (&bv)[CBL], float* eb, int lane,
@@ -156,9 +158,10 @@ __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[RBL][CBL],
         const float4 b = *reinterpret_cast<const float4*>(eb + rr * ER + 8 * q + 4);
         const int64_t m = rb + rr, n = col0 + 8 * q;
         if (m < M && n < N)
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + m * N + n) =
-              make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                         pack_bf16x2(b.z, b.w));
+          __builtin_nontemporal_store(
+              v4i{int(pack_bf16x2(a.x, a.y)), int(pack_bf16x2(a.z, a.w)), int(pack_bf16x2(b.x, b.y)),
+                  int(pack_bf16x2(b.z, b.w))},
+              reinterpret_cast<v4i*>(static_cast<uint16_t*>(Y) + m * N + n));
       }
     } else {
       constexpr int CH = WN / 4;
@@ -169,7 +172,9 @@ __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[RBL][CBL],
         const int rr = lane / CH + RPI * t;
         const float4 a = *reinterpret_cast<const float4*>(eb + rr * ER + 4 * q);
         const int64_t m = rb + rr, n = col0 + 4 * q;
-        if (m < M && n < N) *reinterpret_cast<float4*>(static_cast<float*>(Y) + m * N + n) = a;
+        if (m < M && n < N)
+          __builtin_nontemporal_store(v4f{a.x, a.y, a.z, a.w},
+                                      reinterpret_cast<v4f*>(static_cast<float*>(Y) + m * N + n));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
