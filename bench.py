@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--nbuf", type=int, default=4, help="distinct X / Y buffers rotated")
     ap.add_argument("--no-other-paths", action="store_true",
                     help="skip the NVFP4 and AWQ W4A16 measurements")
-    ap.add_argument("--other-steps", type=int, default=20)
+    ap.add_argument("--other-steps", type=int, default=50)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times "
                          "(a known-size kernel to calibrate rocprofv3 byte counters)")
@@ -166,20 +166,28 @@ def other_paths(steps):
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(svdq.svdq_workspace_bytes(M, K, R, "nvfp4"), dtype=torch.uint8, device=dev)
     codes, scales, lr = svdq.workspace_views(ws, M, K, R, "nvfp4")
-    t_lin = time_calls(lambda i: svdq.svdq_linear_w4a4(x, lay, bias, workspace=ws, Y=y), steps)
-    t_act = time_calls(lambda i: svdq.svdq_act_quantize(x, lay, codes, scales, lr), steps)
-    t_act_loop = time_loop(lambda i: svdq.svdq_act_quantize(x, lay, codes, scales, lr), steps)
-    t_gem = time_calls(lambda i: svdq.svdq_gemm_w4a4(codes, scales, lr, lay, bias, Y=y), steps)
+    # back-to-back loops after a warm-up loop of the same length (the clock
+    # ramps up under load); per-call HIP-event brackets beside them
+    lin = lambda i: svdq.svdq_linear_w4a4(x, lay, bias, workspace=ws, Y=y)
+    act = lambda i: svdq.svdq_act_quantize(x, lay, codes, scales, lr)
+    gem = lambda i: svdq.svdq_gemm_w4a4(codes, scales, lr, lay, bias, Y=y)
+    t_lin_loop = time_loop(lin, steps, warmup=steps)
+    t_act_loop = time_loop(act, steps, warmup=steps)
+    t_gem_loop = time_loop(gem, steps, warmup=steps)
+    t_act = time_calls(act, steps)
+    t_gem = time_calls(gem, steps)
     ops = 2.0 * M * N * K
     act_bytes = M * K * 2 + M * K // 2 + M * K // 16 + M * R * 2 + K * 4 + R * K * 2
     res["nvfp4_mlp_up"] = {
         "workload": "NVFP4 (E2M1 b16, E4M3 block scales), rank 32, M 4608 x K 3072 -> N 12288",
-        "linear_us": round(float(t_lin.mean()) * 1e6, 2),
-        "TOPS": round(ops / t_lin.mean() / 1e12, 1),
-        "gemm_nvfp4": {"avg_us": round(float(t_gem.mean()) * 1e6, 2),
-                       "TFLOP/s": round(ops / t_gem.mean() / 1e12, 1), "bound": "mfma (f16)",
-                       "frac_f16_peak": round(ops / t_gem.mean() / 1e12 / PEAK_F16_TFLOPS, 4),
-                       "frac_fp4_peak": round(ops / t_gem.mean() / 1e12 / PEAK_FP4_TFLOPS, 4)},
+        "linear_us": round(t_lin_loop * 1e6, 2),
+        "TOPS": round(ops / t_lin_loop / 1e12, 1),
+        "timing": "back-to-back loop averages",
+        "gemm_nvfp4": {"avg_us": round(t_gem_loop * 1e6, 2),
+                       "per_call_bracket_us": round(float(t_gem.mean()) * 1e6, 2),
+                       "TFLOP/s": round(ops / t_gem_loop / 1e12, 1), "bound": "mfma (f16)",
+                       "frac_f16_peak": round(ops / t_gem_loop / 1e12 / PEAK_F16_TFLOPS, 4),
+                       "frac_fp4_peak": round(ops / t_gem_loop / 1e12 / PEAK_FP4_TFLOPS, 4)},
         "act_quant_nvfp4": {"avg_us": round(t_act_loop * 1e6, 2),
                             "per_call_bracket_us": round(float(t_act.mean()) * 1e6, 2),
                             "timing": "back-to-back loop average",
@@ -206,14 +214,14 @@ def other_paths(steps):
         y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
         nrot = copies if m <= 64 else 1
         fn = lambda i: svdq.awq_linear_w4a16(x, lays[i % nrot], Y=y)
+        # back-to-back loop average (at the weight-streaming sizes each call
+        # reads a different weight copy), after a warm-up loop
+        t = time_loop(fn, steps, warmup=steps)
         t_call = time_calls(fn, steps)
-        # the weight-streaming sizes run for a few microseconds: their rate
-        # is the back-to-back loop average (each call a different weight copy)
-        t = time_loop(fn, steps) if m <= 64 else float(t_call.mean())
         byts = wbytes + m * K * 2 + m * N * 2
         flops = 2.0 * m * N * K
         r = {"avg_us": round(t * 1e6, 2), "per_call_bracket_us": round(float(t_call.mean()) * 1e6, 2),
-             "timing": "back-to-back loop average" if m <= 64 else "HIP events around each call",
+             "timing": "back-to-back loop average",
              "algorithmic_bytes": byts,
              "GB/s": round(byts / t / 1e9, 1),
              "frac_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4),
@@ -330,12 +338,14 @@ def main():
     torch.cuda.synchronize()
     t_act = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_gemm_loop = time_loop(lambda i: svdq.svdq_gemm_w4a4(codes, scales, lr, layer, bias,
+                                                           Y=ys[i % args.nbuf]), args.steps)
     t_act_loop = time_loop(lambda i: svdq.svdq_act_quantize(xs[i % args.nbuf], layer, codes,
                                                             scales, lr), args.steps)
 
     ops = 2.0 * M * N * K
     value = ops / (ms_step * 1e-3) / 1e12
-    gemm_tops = ops / t_gemm.mean() / 1e12
+    gemm_tops = ops / t_gemm_loop / 1e12
     act_bytes = M * K * 2 + M * K // 2 + M * (K // 64) * 4 + M * R * 2 + K * 4 + R * K * 2
     gemm_bytes = (M * K // 2 + M * (K // 64) * 4 + M * R * 2 + N * K // 2 + N * (K // 64) * 4
                   + N * R * 2 + N * 2 + M * N * 2)
@@ -372,7 +382,7 @@ def main():
             "traffic": traffic,
             "algorithmic_ops_per_launch": ops,
             "algorithmic_bytes_per_launch": gemm_bytes,
-            "avg_launch_us": round(float(t_gemm.mean()) * 1e6, 3),
+            "avg_launch_us": round(t_gemm_loop * 1e6, 3),
         },
         "kernels": {
             "act_quant_int4": {"avg_us": round(t_act_loop * 1e6, 3),
@@ -382,8 +392,10 @@ def main():
                                "algorithmic_bytes": act_bytes,
                                "GB/s": round(act_bytes / t_act_loop / 1e9, 1),
                                "frac_hbm": round(act_bytes / t_act_loop / 1e9 / PEAK_HBM_GBS, 4)},
-            "gemm_int4": {"avg_us": round(float(t_gemm.mean()) * 1e6, 3),
-                          "p95_us": round(float(np.percentile(t_gemm, 95)) * 1e6, 3),
+            "gemm_int4": {"avg_us": round(t_gemm_loop * 1e6, 3),
+                          "timing": "back-to-back loop average",
+                          "per_call_bracket_us": round(float(t_gemm.mean()) * 1e6, 3),
+                          "p95_per_call_bracket_us": round(float(np.percentile(t_gemm, 95)) * 1e6, 3),
                           "TOPS": round(gemm_tops, 2)},
         },
         "gpu": torch.cuda.get_device_name(0),
