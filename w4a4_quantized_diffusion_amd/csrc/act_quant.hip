@@ -536,6 +536,238 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
   lr_reduce_store<RB>(acc, red, row0, M, LR);
 }
 
+// ------------------------------------------------------- 8-row workgroups
+//
+// Used when 16-row workgroups would leave the last round of workgroups mostly
+// idle (M a little above 16 x the CU count): 8 rows per workgroup halve the
+// work unit.  Lane l owns row l % 8 and the 8-element chunk l / 8 of each
+// 64-wide K group.  The 16x16x32 MFMA of the down-projection then sees row
+// l % 16 = row + 8 (chunk & 1) at k-slot chunk / 2: one MFMA with the
+// lora_down chunks 2j gives rows 0..7 the products of the even chunks, a
+// second with the chunks 2j + 1 gives rows 8..15 those of the odd ones, and
+// the row's partial LR is the sum of the two.
+constexpr int ROWS8 = 8;
+
+template <bool XF32>
+struct XRaw8 {
+  uint4 v[XF32 ? 2 : 1];
+};
+
+template <bool XF32>
+__device__ __forceinline__ void load_raw8(const void* X, int64_t off0, XRaw8<XF32>& r) {
+  if constexpr (XF32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(X) + off0);
+    r.v[0] = p[0];
+    r.v[1] = p[1];
+  } else {
+    r.v[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(X) + off0);
+  }
+}
+
+template <bool XF32>
+__device__ __forceinline__ void unpack_raw8(const XRaw8<XF32>& r, bool ok, float (&x)[8],
+                                            uint32_t (&b)[4]) {
+  const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
+  if constexpr (XF32) {
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(&r.v[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(u[j] & keep);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+  } else {
+    const uint32_t w[4] = {r.v[0].x & keep, r.v[0].y & keep, r.v[0].z & keep, r.v[0].w & keep};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b[j] = w[j];
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+struct SmoothRaw8 {
+  float4 v[2];
+};
+
+__device__ __forceinline__ void load_smooth8(const float* __restrict__ smooth, int k0,
+                                             SmoothRaw8& s) {
+  const float4* p = reinterpret_cast<const float4*>(smooth + k0);
+  s.v[0] = p[0];
+  s.v[1] = p[1];
+}
+
+// FP4: NVFP4 codes and E4M3 block scales, else INT4 codes and f32 scales;
+// the same arithmetic as the 16-row kernels, per 8-element chunk
+template <int RB, bool XF32, bool FP4>
+__global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
+    const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
+    const uint16_t* __restrict__ down, const float* __restrict__ ts_x,
+    uint8_t* __restrict__ codes, void* __restrict__ scales, uint16_t* __restrict__ LR) {
+  static_assert(RB <= RB_PREFETCH, "8-row workgroups take the prefetched lora_down path");
+  extern __shared__ float red[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 7, c = lane >> 3;
+  const int64_t row0 = int64_t(blockIdx.x) * ROWS8;
+  const int64_t row = row0 + r;
+  const bool ok = row < M;
+  const int G = K / 64;
+  // LR partials [wave][even / odd chunks][8 rows][R], then the lora_down tiles
+  uint8_t* const dtile = reinterpret_cast<uint8_t*>(red + WAVES * 16 * RB * 16) +
+                         wave * (RB * 16 * DOWN_ROW);
+  float ts = 1.0f, d = 0.0f, rd_hi = 0.0f, rd_lo = 0.0f;
+  bool d_ok = false;
+  if constexpr (FP4) {
+    ts = *ts_x;
+    d = 6.0f * ts;
+    const float rd = __builtin_amdgcn_rcpf(d);
+    rd_hi = rd * PERT_HI;
+    rd_lo = rd * PERT_LO;
+    d_ok = d >= 0x1p-126f && rd < 0x1p126f;
+  }
+  v4f acc_e[RB > 0 ? RB : 1], acc_o[RB > 0 ? RB : 1];
+#pragma unroll
+  for (int i = 0; i < (RB > 0 ? RB : 1); ++i) {
+    acc_e[i] = v4f{0, 0, 0, 0};
+    acc_o[i] = v4f{0, 0, 0, 0};
+  }
+
+  const int T = (G - wave + WAVES - 1) / WAVES;
+  const int64_t xrow = ok ? row : M - 1;
+  XRaw8<XF32> ring[DEPTH];
+  DownRaw<RB> dring[DEPTH];
+  SmoothRaw8 sring[DEPTH];
+  auto fetch = [&](int tt, int sl_) __attribute__((always_inline)) {
+    const int tc = tt < T ? tt : T - 1;
+    const int gg = tc >= 0 ? wave + WAVES * tc : 0;
+    load_raw8<XF32>(X, xrow * K + gg * 64 + 8 * c, ring[sl_]);
+    load_smooth8(smooth, gg * 64 + 8 * c, sring[sl_]);
+    load_down<RB>(down, K, lane, gg * 64, dring[sl_]);
+  };
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
+  for (int t0 = 0; t0 < T; t0 += DEPTH)
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl) {
+    const int t = t0 + sl;
+    const bool live = t < T;
+    const int g = wave + WAVES * (live ? t : T - 1);
+    float x[8];
+    uint32_t b[4];
+    unpack_raw8<XF32>(ring[sl], ok && live, x, b);
+    const float* sm = reinterpret_cast<const float*>(&sring[sl].v[0]);
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = x[j] * sm[j];
+      a = fmaxf(a, fabsf(x[j]));
+    }
+    uint32_t* const cp = reinterpret_cast<uint32_t*>(codes + (int64_t(g) * M + row) * 32);
+    if constexpr (!FP4) {
+      // INT4 group of 64: the row's eight chunks are lanes r, r + 8, ...
+      a = fmaxf(a, __shfl_xor(a, 8));
+      a = fmaxf(a, __shfl_xor(a, 16));
+      a = fmaxf(a, __shfl_xor(a, 32));
+      const float s = a / 7.0f;
+      const float inv = 1.0f / s;
+      const bool fast = s >= 0x1p-126f;
+      uint32_t w = 0;
+      if (s > 0.f) {
+        float tq[8], rq[8];
+        bool need = !fast;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          tq[j] = x[j] * inv;
+          rq[j] = rintf(fabsf(tq[j]));
+          need |= near_half_r(tq[j], rq[j]);
+        }
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (!fast || near_half_r(tq[j], rq[j])) {
+              tq[j] = x[j] / s;
+              rq[j] = rintf(fabsf(tq[j]));
+            }
+        }
+        w = int4_word(tq, rq);
+      }
+      if (ok && live) {
+        cp[c] = w;
+        if (c == 0) static_cast<float*>(scales)[int64_t(g) * M + row] = s;
+      }
+    } else {
+      // NVFP4 block of 16: chunks c and c ^ 1, lanes l and l ^ 8
+      a = fmaxf(a, __shfl_xor(a, 8));
+      const uint32_t sb = e4m3_block_scale(a, d, rd_hi, rd_lo, d_ok);
+      const float den = __builtin_amdgcn_cvt_f32_fp8(int(sb), 0) * ts;
+      uint32_t w = 0;
+      if (den > 0.f) {
+        const float inv = __builtin_amdgcn_rcpf(den);
+        const bool fast = den >= 0x1p-126f && inv < 0x1p126f;
+        uint32_t ev, od;
+        e2m1_pairs(x, inv * PERT_HI, inv * PERT_LO, ev, od);
+        const uint32_t differ = ((ev ^ (ev >> 4)) | (od ^ (od >> 4))) & 0x0F0F0F0Fu;
+        uint32_t word = (ev & 0x0F0F0F0Fu) | ((od & 0x0F0F0F0Fu) << 4);
+        if (__builtin_amdgcn_ballot_w64(differ != 0 || !fast) != 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t src = (j & 1) ? od : ev;
+            const uint32_t byte = src >> (8 * (j >> 1));
+            if (!fast || ((byte ^ (byte >> 4)) & 15u) != 0) {
+              const uint32_t cj = e2m1_rne_sat(x[j] / den);
+              word = (word & ~(15u << (4 * j))) | (cj << (4 * j));
+            }
+          }
+        }
+        w = e2m1_clear_negzero(word);
+      }
+      if (ok && live) {
+        cp[c] = w;
+        if ((c & 1) == 0)
+          static_cast<uint8_t*>(scales)[(int64_t(g) * M + row) * 4 + (c >> 1)] = uint8_t(sb);
+      }
+    }
+    if constexpr (RB > 0) {
+      stage_down<RB>(dtile, lane, dring[sl]);
+      const v4i ai = {int(b[0]), int(b[1]), int(b[2]), int(b[3])};
+      const v8bf av = __builtin_bit_cast(v8bf, ai);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint8_t* tr = dtile + (rb * 16 + (lane & 15)) * DOWN_ROW + (lane >> 4) * 32;
+        const uint4 be = *reinterpret_cast<const uint4*>(tr);
+        const uint4 bo = *reinterpret_cast<const uint4*>(tr + 16);
+        const v4i bei = {int(be.x), int(be.y), int(be.z), int(be.w)};
+        const v4i boi = {int(bo.x), int(bo.y), int(bo.z), int(bo.w)};
+        acc_e[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, bei),
+                                                            acc_e[rb], 0, 0, 0);
+        acc_o[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, boi),
+                                                            acc_o[rb], 0, 0, 0);
+      }
+    }
+    fetch(t + DEPTH, sl);
+  }
+  if constexpr (RB > 0) {
+    constexpr int R = RB * 16;
+    // 16x16 f32 MFMA result: lane l holds column l%16, rows 4(l/16) + j; the
+    // even-chunk sums are rows 0..7 (lanes 0..31), the odd ones rows 8..15
+    const int half = lane >> 5;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        red[((wave * 2 + half) * 8 + 4 * ((lane >> 4) & 1) + j) * R + rb * 16 + (lane & 15)] =
+            half ? acc_o[rb][j] : acc_e[rb][j];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS8 * R; idx += blockDim.x) {
+      const int rr = idx / R, cc = idx % R;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 2 * WAVES; ++w) sum += red[(w * 8 + rr) * R + cc];
+      if (row0 + rr < M) LR[(row0 + rr) * R + cc] = f32_to_bf16(sum);
+    }
+  }
+}
+
 template <template <int, bool> class Launcher, int RB>
 struct RankDispatch {
   template <typename... A>
@@ -545,6 +777,31 @@ struct RankDispatch {
     return svdq::fail(SVDQ_ERR_UNSUPPORTED, "rank must be a multiple of 16, at most 256");
   }
 };
+
+// compute units of the current device (cached per device; 0 if unknown)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Whether 8-row workgroups finish sooner than 16-row ones: with one
+// workgroup per CU, the time goes as (rounds of workgroups) x (rows each).
+bool use_rows8(int M, int RB) {
+  const int cus = cu_count();
+  if (RB > RB_PREFETCH || cus <= 0) return false;
+  auto cost = [&](int rows) {
+    const int64_t wgs = (int64_t(M) + rows - 1) / rows;
+    return (wgs + cus - 1) / cus * rows;
+  };
+  return cost(ROWS8) < cost(ROWS);
+}
 
 // LR reduction buffer, then (small ranks) the waves' lora_down tiles
 constexpr size_t lds_bytes(int RB) {
@@ -559,6 +816,15 @@ struct Int4Launch {
                         const uint16_t* down, uint8_t* codes, float* scales, uint16_t* LR,
                         hipStream_t s) {
     const size_t shm = lds_bytes(RB);
+    if constexpr (RB <= RB_PREFETCH) {
+      static_assert(lds_bytes(RB_PREFETCH) <= 65536, "no dynamic-LDS opt-in on this path");
+      if (use_rows8(M, RB)) {
+        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XF32, false>), dim3((M + ROWS8 - 1) / ROWS8),
+                           dim3(64 * WAVES), shm, s, X, M, K, smooth, down, nullptr, codes,
+                           static_cast<void*>(scales), LR);
+        return svdq::check_launch("act_quant_int4");
+      }
+    }
     if (shm > 65536 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_int4_kernel<RB, XF32>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
@@ -576,6 +842,14 @@ struct Fp4Launch {
                         const uint16_t* down, const float* ts_x, uint8_t* codes,
                         uint8_t* scales, uint16_t* LR, hipStream_t s) {
     const size_t shm = lds_bytes(RB);
+    if constexpr (RB <= RB_PREFETCH) {
+      if (use_rows8(M, RB)) {
+        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XF32, true>), dim3((M + ROWS8 - 1) / ROWS8),
+                           dim3(64 * WAVES), shm, s, X, M, K, smooth, down, ts_x, codes,
+                           static_cast<void*>(scales), LR);
+        return svdq::check_launch("act_quant_nvfp4");
+      }
+    }
     if (shm > 65536 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_nvfp4_kernel<RB, XF32>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
