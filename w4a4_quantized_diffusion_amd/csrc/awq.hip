@@ -136,10 +136,10 @@ __global__ __launch_bounds__(SK_NT) void awq_skinny_kernel(
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) fetch(d, ring[d]);
-  for (int t0 = 0; t0 < T; t0 += D)
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int tt = t0 + d;
+  // process slot d of the ring for chunk tt; refill it with chunk tt + D
+  // only when some wave of the launch has chunks past the first D (else the
+  // refills would all repeat the last chunk)
+  auto consume = [&](int tt, int d, bool refill) __attribute__((always_inline)) {
       const bool live = tt < T;
       SkinnySlot<MT>& sl = ring[d];
       uint4 b[SK_TILES][2];
@@ -161,8 +161,16 @@ __global__ __launch_bounds__(SK_NT) void awq_skinny_kernel(
                 __builtin_bit_cast(v8bf, sl.x[mt][hh]), __builtin_bit_cast(v8bf, b[t][hh]),
                 acc[mt][t], 0, 0, 0);
       }
-      fetch(tt + D, sl);
-    }
+      if (refill) fetch(tt + D, sl);
+  };
+  if (G > SK_WAVES * D) {
+    for (int t0 = 0; t0 < T; t0 += D)
+#pragma unroll
+      for (int d = 0; d < D; ++d) consume(t0 + d, d, true);
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d) consume(d, d, false);
+  }
   // fixed-order reduction of the 8 waves' partial sums through LDS:
   // waves 4..7 into 0..3, then 1..3 into 0
   auto put = [&](int slot) __attribute__((always_inline)) {
