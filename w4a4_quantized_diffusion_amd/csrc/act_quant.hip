@@ -14,17 +14,21 @@
 //
 // Work split: a workgroup of 8 waves owns 16 rows; wave w takes the K-groups
 // w, w+8, ... so that at every step the 8 waves read adjacent 128-byte
-// pieces of each row, and keeps the X loads of its next 3 groups in flight
-// (the kernel is bound by reading X).  Lane l owns row (l % 16) and the two
-// 8-element chunks k = 64g + 8(l/16) + [0, 8) and +32: exactly the A-operand slice of
-// a 16x16x32 bf16 MFMA, so the down-projection needs no data movement.
+// pieces of each row, and keeps the X loads of its next 3 groups in flight.
+// Lane l owns row (l % 16) and the two 8-element chunks
+// k = 64g + 8(l/16) + [0, 8) and +32: exactly the A-operand slice of a
+// 16x16x32 bf16 MFMA, so the down-projection needs no data movement of X.
 // The per-wave LR partial sums are reduced in a fixed order through LDS
-// (deterministic).
+// (deterministic).  Where 16-row workgroups would leave the last round of
+// workgroups mostly idle, 8-row workgroups take the same steps (see the
+// 8-row kernel below).
 //
-// The quantizer divides with IEEE semantics: q = rne(fl32(Xh / s)).  It
-// computes t = Xh * fl32(1/s) (within 2^-20 of the quotient for |q| <= 7) and
-// only when t lies within 2^-19 of a half-integer repeats the exact division,
-// so the code is always the one the correctly rounded quotient gives.
+// The quantizers divide with IEEE semantics: q = rne(fl32(Xh / s)) for INT4,
+// the E4M3 / E2M1 roundings of fl32 quotients for NVFP4.  They compute the
+// quotients through a reciprocal and repeat the exact division only for the
+// values that could round differently (a wave ballot skips the repeat when
+// no lane needs it), so every code is the one the correctly rounded
+// quotient gives.
 
 #include "internal.h"
 
