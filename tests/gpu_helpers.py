@@ -129,3 +129,24 @@ def assert_y_close(y_gpu, y_ref, bf16_out, what=""):
     assert not bad.any(), (f"{what}: {bad.sum()} elements out of tolerance; "
                            f"max err {err.max():.3e}, rms(Y) {np.sqrt(np.mean(y_ref ** 2)):.3e}")
     return float(err.max() / np.sqrt(np.mean(y_ref ** 2)))
+
+
+def degenerate_activations(seed=0, k=256, m=24):
+    """fp32 activations that hit the quantizers' special cases: an all-zero
+    row, all-zero / constant / subnormal / huge (1e30) groups, one outlier in
+    a group of zeros, groups of equal magnitudes, and rows scaled by 10^e for
+    e in [-40, 30] (scales that underflow to zero or become subnormal)."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((m, k)).astype(np.float32)
+    x[0] = 0
+    x[1, 0:64] = 0
+    x[1, 64:128] = 3.0
+    x[1, 128:192] = (g.choice([-1, 1], 64) * 1e-42).astype(np.float32)
+    x[1, 192:256] = (g.standard_normal(64) * 1e30).astype(np.float32)
+    x[2] = 0
+    for b in range(k // 16):
+        x[2, 16 * b + (b * 5) % 16] = 5.0 if b % 2 else -5.0
+    x[3] = np.where(g.integers(0, 2, k) == 1, 2.5, -2.5).astype(np.float32)
+    for r in range(4, m):
+        x[r] *= np.float32(10.0 ** g.uniform(-40, 30))
+    return x

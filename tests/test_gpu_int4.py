@@ -14,7 +14,7 @@ from oracle import formats as F
 from w4a4_quantized_diffusion_amd import svdq, synth
 from tests.gpu_helpers import (t_f32, t_x, t_u8, t_bf16_bits, layer_to_device,
                                random_int4_layer, bf16_bits_np, assert_lr_close, assert_y_close,
-                               gm_codes, rm_codes, gm_scales)
+                               gm_codes, rm_codes, gm_scales, degenerate_activations)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,18 @@ def test_act_quant_half_integer_ties():
             x[r, 64 * g] = 7 * s if (r + g) % 3 else -7 * s
             for i in range(1, 64):
                 x[r, 64 * g + i] = vals[(r * 5 + g * 11 + i) % vals.size]
+    lay = dict(smooth=np.ones(k, np.float32), q=np.zeros((16, k), np.int8),
+               wcodes=np.zeros((16, k // 2), np.uint8), sW=np.ones((16, k // 64), np.float32),
+               lora_down=None, lora_up=None)
+    _check_act(x, lay, 0, bf16=False)
+
+
+def test_act_quant_degenerate_inputs():
+    """All-zero rows and groups (scale 0, codes 0), constant groups, subnormal
+    and huge values, scales that underflow or are subnormal (the exact
+    division path): codes and scales bit-exact against the oracle."""
+    x = degenerate_activations(seed=3)
+    k = x.shape[1]
     lay = dict(smooth=np.ones(k, np.float32), q=np.zeros((16, k), np.int8),
                wcodes=np.zeros((16, k // 2), np.uint8), sW=np.ones((16, k // 64), np.float32),
                lora_down=None, lora_up=None)

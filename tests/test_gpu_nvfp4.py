@@ -14,7 +14,8 @@ from oracle import nvfp4 as O4
 from oracle import formats as F
 from w4a4_quantized_diffusion_amd import svdq, synth
 from tests.gpu_helpers import (t_f32, t_x, t_u8, t_bf16_bits, random_int4_layer,
-                               assert_lr_close, assert_y_close, gm_codes, rm_codes)
+                               assert_lr_close, assert_y_close, gm_codes, rm_codes,
+                               degenerate_activations)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,6 +117,19 @@ def test_nvfp4_act_quant_block_scale_ties():
         blk[(i * 7) % 16] = v if i % 2 else -v
         x[r, 16 * b_:16 * b_ + 16] = blk
     lay = dict(smooth=np.ones(k, np.float32), ts_x=np.float32(1.0), ts_w=np.float32(1.0),
+               codes=np.zeros((16, k), np.uint8), sbw=np.zeros((16, k // 16), np.uint8),
+               lora_down=None, lora_up=None)
+    _check_act(x, lay, 0, bf16=False)
+
+
+@pytest.mark.parametrize("ts", [1.0, 3.0e-5])
+def test_nvfp4_act_quant_degenerate_inputs(ts):
+    """All-zero rows and blocks, constant blocks, subnormal and huge values,
+    block scales that round to zero or saturate at 448: codes and scales
+    bit-exact against the oracle, for two tensor scales."""
+    x = degenerate_activations(seed=4)
+    k = x.shape[1]
+    lay = dict(smooth=np.ones(k, np.float32), ts_x=np.float32(ts), ts_w=np.float32(1.0),
                codes=np.zeros((16, k), np.uint8), sbw=np.zeros((16, k // 16), np.uint8),
                lora_down=None, lora_up=None)
     _check_act(x, lay, 0, bf16=False)
