@@ -88,17 +88,19 @@ struct Packed {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-typedef int v2i_t __attribute__((ext_vector_type(2)));
-
-// LDS stores at a compile-time byte offset from one address register
+// LDS stores at a compile-time byte offset from one address register (a
+// 16-byte store per pair of words: with 80-byte rows the 16 lanes of one
+// store phase hit distinct banks)
 template <int OFF>
-__device__ __forceinline__ void lds_store_b64(uint32_t addr, v2i_t d) {
-  asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF));
+__device__ __forceinline__ void lds_store_b128(uint32_t addr, v4i d) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF));
 }
-__device__ __forceinline__ v2i_t widen8(uint32_t word) {
-  uint32_t lo, hi;
-  nib8_to_e4m3(word, lo, hi);
-  return v2i_t{int(lo), int(hi)};
+// two packed words -> their 16 widened bytes
+__device__ __forceinline__ v4i widen16(uint32_t w0, uint32_t w1) {
+  uint32_t l0, h0, l1, h1;
+  nib8_to_e4m3(w0, l0, h0);
+  nib8_to_e4m3(w1, l1, h1);
+  return v4i{int(l0), int(h0), int(l1), int(h1)};
 }
 
 template <typename T>
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
         uint32_t(reinterpret_cast<uintptr_t>((lds_cptr)&pk.code[wave][lane * 32 + half * 16]));
     asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(w) : "v"(addr));
   };
-  // widen packed word `word` (index w) into 8 E4M3 bytes at LDS offset 8w
+  // widen packed words 2p, 2p+1 into 16 E4M3 bytes at LDS offset 16p
   // LDS stores of the widened codes / scales go through asm as well:
   // the compiler would wait for every DMA in flight before any LDS store.
   typedef __attribute__((address_space(3))) uint8_t* lds_bptr;
@@ -198,14 +200,10 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     v4i w0, w1;
     fetch_words(pk, w0, w1);
     const uint32_t a = lds_addr(stage_base + soff);
-    lds_store_b64<0>(a, widen8(uint32_t(w0[0])));
-    lds_store_b64<8>(a, widen8(uint32_t(w0[1])));
-    lds_store_b64<16>(a, widen8(uint32_t(w0[2])));
-    lds_store_b64<24>(a, widen8(uint32_t(w0[3])));
-    lds_store_b64<32>(a, widen8(uint32_t(w1[0])));
-    lds_store_b64<40>(a, widen8(uint32_t(w1[1])));
-    lds_store_b64<48>(a, widen8(uint32_t(w1[2])));
-    lds_store_b64<56>(a, widen8(uint32_t(w1[3])));
+    lds_store_b128<0>(a, widen16(uint32_t(w0[0]), uint32_t(w0[1])));
+    lds_store_b128<16>(a, widen16(uint32_t(w0[2]), uint32_t(w0[3])));
+    lds_store_b128<32>(a, widen16(uint32_t(w1[0]), uint32_t(w1[1])));
+    lds_store_b128<48>(a, widen16(uint32_t(w1[2]), uint32_t(w1[3])));
   };
   // the same, spread over the MFMA blocks: word pair p = 0..3
   v4i pw;
@@ -213,20 +211,16 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     const uint32_t a = lds_addr(stage_base + soff);
     switch (p) {
       case 0:
-        lds_store_b64<0>(a, widen8(uint32_t(pw[0])));
-        lds_store_b64<8>(a, widen8(uint32_t(pw[1])));
+        lds_store_b128<0>(a, widen16(uint32_t(pw[0]), uint32_t(pw[1])));
         break;
       case 1:
-        lds_store_b64<16>(a, widen8(uint32_t(pw[2])));
-        lds_store_b64<24>(a, widen8(uint32_t(pw[3])));
+        lds_store_b128<16>(a, widen16(uint32_t(pw[2]), uint32_t(pw[3])));
         break;
       case 2:
-        lds_store_b64<32>(a, widen8(uint32_t(pw[0])));
-        lds_store_b64<40>(a, widen8(uint32_t(pw[1])));
+        lds_store_b128<32>(a, widen16(uint32_t(pw[0]), uint32_t(pw[1])));
         break;
       default:
-        lds_store_b64<48>(a, widen8(uint32_t(pw[2])));
-        lds_store_b64<56>(a, widen8(uint32_t(pw[3])));
+        lds_store_b128<48>(a, widen16(uint32_t(pw[2]), uint32_t(pw[3])));
         break;
     }
   };
