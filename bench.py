@@ -147,10 +147,13 @@ def time_loop(fn, steps, warmup=3):
 
 def other_paths(steps):
     """The NVFP4 precision at the MLP up-projection shape (M 4608, K 3072 ->
-    N 12288, rank 32) and the AWQ W4A16 layer (K 3072 -> N 12288) at M = 1,
-    16 and 4608: seeded synthetic tensors, weights quantized by the library,
-    per-kernel HIP-event times.  Weight-streaming cases rotate enough weight
-    copies (> 512 MB) that the 256 MB last-level cache cannot hold them."""
+    N 12288, rank 32), the INT4 MLP down-projection with the GELU fused in
+    (M 4608, K 12288 -> N 3072) and the AWQ W4A16 layer (K 3072 -> N 12288) at M = 1,
+    16 and 4608: seeded synthetic tensors, weights quantized by the library
+    (the down-projection's INT4 layer drawn directly), per-kernel HIP-event
+    times.  Weight-streaming cases rotate enough weight copies (> 512 MB)
+    that the 256 MB last-level cache cannot hold them."""
+    import numpy as np
     import torch
     from w4a4_quantized_diffusion_amd import svdq, synth
     dev = torch.device("cuda:0")
@@ -194,6 +197,46 @@ def other_paths(steps):
                             "algorithmic_bytes": act_bytes,
                             "GB/s": round(act_bytes / t_act_loop / 1e9, 1),
                             "frac_hbm": round(act_bytes / t_act_loop / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    del x, lay, y, ws, codes, scales, lr
+    torch.cuda.empty_cache()
+
+    # INT4 MLP down-projection with the GELU fused into the activation pass
+    M, K, N, R = 4608, 12288, 3072, 32
+    mw = synth.WORKLOADS["mlp"]
+    x = torch.from_numpy(synth.activations(M, K, 0, mw, 0)).to(dev).to(torch.bfloat16)
+    r = synth.random_int4_layer(N, K, R, 0, "mlp")
+    lay = dict(rank=R, prec=svdq.INT4, N=N, K=K, smooth=torch.from_numpy(r["smooth"]).to(dev),
+               lora_down=torch.from_numpy(r["lora_down_bits"].view("int16")).to(dev),
+               lora_up=torch.from_numpy(r["lora_up_bits"].view("int16")).to(dev),
+               wcodes=torch.from_numpy(np.ascontiguousarray(
+                   r["wcodes"].reshape(N, K // 64, 32).transpose(1, 0, 2))).to(dev),
+               wscales=torch.from_numpy(np.ascontiguousarray(r["sW"].T)).to(dev),
+               w_tensor_scale=torch.ones(1, device=dev), x_tensor_scale=torch.ones(1, device=dev))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(svdq.svdq_workspace_bytes(M, K, R), dtype=torch.uint8, device=dev)
+    codes, scales, lr = svdq.workspace_views(ws, M, K, R)
+    t_lin_g = time_loop(lambda i: svdq.svdq_linear_w4a4_gelu(x, lay, workspace=ws, Y=y), steps,
+                        warmup=steps)
+    t_lin_p = time_loop(lambda i: svdq.svdq_linear_w4a4(x, lay, workspace=ws, Y=y), steps,
+                        warmup=steps)
+    t_act_g = time_loop(lambda i: svdq.svdq_act_quantize_gelu(x, lay, codes, scales, lr), steps,
+                        warmup=steps)
+    t_act_p = time_loop(lambda i: svdq.svdq_act_quantize(x, lay, codes, scales, lr), steps,
+                        warmup=steps)
+    ops = 2.0 * M * N * K
+    act_bytes = M * K * 2 + M * K // 2 + M * (K // 64) * 4 + M * R * 2 + K * 4 + R * K * 2
+    res["int4_mlp_down_gelu"] = {
+        "workload": "INT4 g64, rank 32, GELU fused into the activation pass, "
+                    "M 4608 x K 12288 -> N 3072",
+        "timing": "back-to-back loop averages",
+        "linear_us": round(t_lin_g * 1e6, 2),
+        "TOPS": round(ops / t_lin_g / 1e12, 1),
+        "linear_without_gelu_us": round(t_lin_p * 1e6, 2),
+        "act_quant_gelu_us": round(t_act_g * 1e6, 2),
+        "act_quant_us": round(t_act_p * 1e6, 2),
+        "act_quant_gelu_frac_hbm": round(act_bytes / t_act_g / 1e9 / PEAK_HBM_GBS, 4),
+        "unfused_gelu_pass_bytes": 2 * M * K * 2,
     }
     del x, lay, y, ws, codes, scales, lr
     torch.cuda.empty_cache()

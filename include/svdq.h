@@ -188,6 +188,30 @@ svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64
                              void* Y, svdq_dtype y_dtype, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* The MLP down-projection's input form: the same calls with X replaced by
+ * GELU(X), fused into the activation pass (the original engine's fused
+ * GELU / MLP kernels: chaosnode.de page, "Nunchaku Lite vs. Original").
+ *   X' = bf16(gelu(X)),  gelu(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+ * (the tanh form, evaluated in fp32 as x / (1 + exp(-2u)) with the hardware
+ * exp2 and reciprocal, a few ulps, and rounded to bf16: the value an unfused
+ * GELU would store); X' then feeds the smoothing, quantization and
+ * low-rank down-projection exactly as X does in svdq_act_quantize.
+ * x_dtype must be SVDQ_BF16 (else SVDQ_ERR_UNSUPPORTED); other arguments,
+ * layouts and errors as svdq_act_quantize / svdq_linear_w4a4. */
+svdq_status svdq_act_quantize_gelu(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                                   int32_t rank, svdq_precision prec, const float* smooth,
+                                   const uint16_t* lora_down, const float* x_tensor_scale,
+                                   uint8_t* codes, void* scales, uint16_t* LR,
+                                   hipStream_t stream);
+svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                                  int64_t N, int32_t rank, svdq_precision prec,
+                                  const float* smooth, const uint16_t* lora_down,
+                                  const uint16_t* lora_up, const uint8_t* wcodes,
+                                  const void* wscales, const float* w_tensor_scale,
+                                  const float* x_tensor_scale, const void* bias,
+                                  void* Y, svdq_dtype y_dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* Offline AWQ W4A16 quantization (asymmetric INT4, the awq_w4a16 row of the
  * "Hardware-Support" table).  Per output row and group of `group` along K:
  *   mn = min(min w, 0), mx = max(max w, 0), s = bf16(fl32(fl32(mx - mn) / 15))

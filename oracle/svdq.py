@@ -272,3 +272,22 @@ def output_f32(y):
 
 def output_bf16_bits(y):
     return bf16_bits(fl32(y))
+
+
+# ---------------------------------------------------------------- GELU input
+
+def gelu_tanh(x):
+    """GELU in its tanh form, the feed-forward activation between the MLP up-
+    and down-projections (the original engine fuses it into its MLP kernels:
+    chaosnode.de page, "Nunchaku Lite vs. Original"), in float64:
+    0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    x = np.asarray(x, dtype=F64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def gelu_input(x):
+    """The down-projection's input with GELU fused into the activation step:
+    X' = bf16(gelu(X)) for bf16 X, the value an unfused GELU would store (fp32
+    evaluation, then bf16).  Returns float32 values that are bf16 values."""
+    return bf16(gelu_tanh(x)).astype(np.float32)
+

@@ -140,3 +140,19 @@ def test_smoke_inputs_are_contiguous():
     for k, v in layer.items():
         if hasattr(v, "is_contiguous"):
             assert v.is_contiguous(), k
+
+
+def test_gelu_forms_take_bf16_only(lib):
+    # x_dtype 0 is f32: the GELU input form rejects it before touching anything
+    st = lib.svdq_act_quantize_gelu(None, 0, 64, 128, 16, 0, None, None, None, None, None, None,
+                                    None)
+    assert st == UNSUPPORTED and "bf16" in svdq.svdq_last_error()
+    st = lib.svdq_linear_w4a4_gelu(None, 0, 64, 128, 64, 16, 0, None, None, None, None, None,
+                                   None, None, None, None, 1, None, 0, None)
+    assert st == UNSUPPORTED and "bf16" in svdq.svdq_last_error()
+    # bf16 with bad shapes / NULL pointers: the usual validation
+    st = lib.svdq_act_quantize_gelu(None, 1, 64, 100, 16, 0, None, None, None, None, None, None,
+                                    None)
+    assert st == INVALID and "K must" in svdq.svdq_last_error()
+    assert lib.svdq_act_quantize_gelu(None, 1, 0, 128, 16, 0, None, None, None, None, None, None,
+                                      None) == 0

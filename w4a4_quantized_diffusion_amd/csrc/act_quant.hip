@@ -134,6 +134,38 @@ __device__ __forceinline__ void unpack_raw(const XRaw<XF32>& r, bool ok, float (
   }
 }
 
+// The input of the MLP down-projection is GELU of the up-projection's bf16
+// output; the fused form applies it here, per element: the tanh form
+// 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3), evaluated as
+// x / (1 + exp(-2u)) in fp32 with the hardware exp2 and reciprocal (a few
+// ulps) and rounded to bf16 (the value an unfused GELU would have stored).
+// The fused GELU / MLP kernels of the original engine: chaosnode.de page,
+// "Nunchaku Lite vs. Original".
+__device__ __forceinline__ float gelu_f32(float x) {
+  // exp(-2u) = 2^(-2 log2(e) sqrt(2/pi) (x + 0.044715 x^3)); 1 / (1 + inf) = 0
+  // gives -0 far out
+  const float e = __builtin_amdgcn_exp2f(-2.302208198144325f * fmaf(0.044715f * x, x * x, x));
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+typedef float gelu_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 gelu_b2 __attribute__((ext_vector_type(2)));
+
+// GELU of 2n values in place, rounded to bf16 (v_cvt_pk_bf16_f32, nearest
+// even), and their bf16 pairs for the down-projection
+template <int N>
+__device__ __forceinline__ void gelu_chunk(float (&x)[N], uint32_t (&b)[N / 2]) {
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    const uint32_t p = __builtin_bit_cast(
+        uint32_t, __builtin_convertvector(gelu_f2{gelu_f32(x[2 * j]), gelu_f32(x[2 * j + 1])},
+                                          gelu_b2));
+    b[j] = p;
+    x[2 * j] = __uint_as_float(p << 16);
+    x[2 * j + 1] = __uint_as_float(p & 0xFFFF0000u);
+  }
+}
+
 // The smooth factors of one lane's two 8-element chunks, fetched with the
 // X loads of the same group (a load issued later would be counted behind
 // every X load in flight and have to wait for all of them).
@@ -295,12 +327,14 @@ __device__ __forceinline__ void lr_reduce_store(v4f (&acc)[RB > 0 ? RB : 1], flo
   }
 }
 
-template <int RB, bool XF32>
+// XIN: 0 bf16 X, 1 f32 X, 2 bf16 X through GELU first
+template <int RB, int XIN>
 __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ down, uint8_t* __restrict__ codes,
     float* __restrict__ scales, uint16_t* __restrict__ LR) {
   extern __shared__ float red[];
+  constexpr bool XF32 = XIN == 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -347,6 +381,10 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     float x0[8], x1[8], s0[8], s1[8];
     uint32_t b0[4], b1[4];
     unpack_raw<XF32>(ring[sl], ok && live, x0, x1, b0, b1);
+    if constexpr (XIN == 2) {
+      gelu_chunk<8>(x0, b0);
+      gelu_chunk<8>(x1, b1);
+    }
     unpack_smooth(sring[sl], s0, s1);
     float amax = 0.f;
 #pragma unroll
@@ -416,12 +454,13 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
 
 // ---------------------------------------------------------------- NVFP4
 
-template <int RB, bool XF32>
+template <int RB, int XIN>
 __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
     const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ down, const float* __restrict__ ts_x,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ LR) {
   extern __shared__ float red[];
+  constexpr bool XF32 = XIN == 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -471,6 +510,10 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
     float x0[8], x1[8], s0[8], s1[8];
     uint32_t b0[4], b1[4];
     unpack_raw<XF32>(ring[sl], ok && live, x0, x1, b0, b1);
+    if constexpr (XIN == 2) {
+      gelu_chunk<8>(x0, b0);
+      gelu_chunk<8>(x1, b1);
+    }
     unpack_smooth(sring[sl], s0, s1);
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -602,13 +645,14 @@ __device__ __forceinline__ void load_smooth8(const float* __restrict__ smooth, i
 
 // FP4: NVFP4 codes and E4M3 block scales, else INT4 codes and f32 scales;
 // the same arithmetic as the 16-row kernels, per 8-element chunk
-template <int RB, bool XF32, bool FP4>
+template <int RB, int XIN, bool FP4>
 __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
     const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ down, const float* __restrict__ ts_x,
     uint8_t* __restrict__ codes, void* __restrict__ scales, uint16_t* __restrict__ LR) {
   static_assert(RB <= RB_PREFETCH, "8-row workgroups take the prefetched lora_down path");
   extern __shared__ float red[];
+  constexpr bool XF32 = XIN == 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 7, c = lane >> 3;
@@ -659,6 +703,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
     float x[8];
     uint32_t b[4];
     unpack_raw8<XF32>(ring[sl], ok && live, x, b);
+    if constexpr (XIN == 2) gelu_chunk<8>(x, b);
     const float* sm = reinterpret_cast<const float*>(&sring[sl].v[0]);
     float a = 0.f;
 #pragma unroll
@@ -772,12 +817,14 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
   }
 }
 
-template <template <int, bool> class Launcher, int RB>
+template <template <int, int> class Launcher, int RB>
 struct RankDispatch {
   template <typename... A>
-  static svdq_status run(int rb, bool f32, A... args) {
-    if (rb == RB) return f32 ? Launcher<RB, true>::go(args...) : Launcher<RB, false>::go(args...);
-    if constexpr (RB < 16) return RankDispatch<Launcher, RB + 1>::run(rb, f32, args...);
+  static svdq_status run(int rb, int xin, A... args) {
+    if (rb == RB)
+      return xin == 1 ? Launcher<RB, 1>::go(args...)
+                      : (xin == 2 ? Launcher<RB, 2>::go(args...) : Launcher<RB, 0>::go(args...));
+    if constexpr (RB < 16) return RankDispatch<Launcher, RB + 1>::run(rb, xin, args...);
     return svdq::fail(SVDQ_ERR_UNSUPPORTED, "rank must be a multiple of 16, at most 256");
   }
 };
@@ -814,7 +861,7 @@ constexpr size_t lds_bytes(int RB) {
                 : 0;
 }
 
-template <int RB, bool XF32>
+template <int RB, int XIN>
 struct Int4Launch {
   static svdq_status go(const void* X, int M, int K, const float* smooth,
                         const uint16_t* down, uint8_t* codes, float* scales, uint16_t* LR,
@@ -823,24 +870,24 @@ struct Int4Launch {
     if constexpr (RB <= RB_PREFETCH) {
       static_assert(lds_bytes(RB_PREFETCH) <= 65536, "no dynamic-LDS opt-in on this path");
       if (use_rows8(M, RB)) {
-        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XF32, false>), dim3((M + ROWS8 - 1) / ROWS8),
+        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XIN, false>), dim3((M + ROWS8 - 1) / ROWS8),
                            dim3(64 * WAVES), shm, s, X, M, K, smooth, down, nullptr, codes,
                            static_cast<void*>(scales), LR);
         return svdq::check_launch("act_quant_int4");
       }
     }
     if (shm > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_int4_kernel<RB, XF32>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_int4_kernel<RB, XIN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
       return svdq::fail(SVDQ_ERR_HIP, "act_quant_int4: shared memory size");
     dim3 grid((M + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((act_quant_int4_kernel<RB, XF32>), grid, dim3(64 * WAVES), shm, s, X, M,
+    hipLaunchKernelGGL((act_quant_int4_kernel<RB, XIN>), grid, dim3(64 * WAVES), shm, s, X, M,
                        K, smooth, down, codes, scales, LR);
     return svdq::check_launch("act_quant_int4");
   }
 };
 
-template <int RB, bool XF32>
+template <int RB, int XIN>
 struct Fp4Launch {
   static svdq_status go(const void* X, int M, int K, const float* smooth,
                         const uint16_t* down, const float* ts_x, uint8_t* codes,
@@ -848,18 +895,18 @@ struct Fp4Launch {
     const size_t shm = lds_bytes(RB);
     if constexpr (RB <= RB_PREFETCH) {
       if (use_rows8(M, RB)) {
-        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XF32, true>), dim3((M + ROWS8 - 1) / ROWS8),
+        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XIN, true>), dim3((M + ROWS8 - 1) / ROWS8),
                            dim3(64 * WAVES), shm, s, X, M, K, smooth, down, ts_x, codes,
                            static_cast<void*>(scales), LR);
         return svdq::check_launch("act_quant_nvfp4");
       }
     }
     if (shm > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_nvfp4_kernel<RB, XF32>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_nvfp4_kernel<RB, XIN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
       return svdq::fail(SVDQ_ERR_HIP, "act_quant_nvfp4: shared memory size");
     dim3 grid((M + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((act_quant_nvfp4_kernel<RB, XF32>), grid, dim3(64 * WAVES), shm, s, X,
+    hipLaunchKernelGGL((act_quant_nvfp4_kernel<RB, XIN>), grid, dim3(64 * WAVES), shm, s, X,
                        M, K, smooth, down, ts_x, codes, scales, LR);
     return svdq::check_launch("act_quant_nvfp4");
   }
@@ -890,21 +937,23 @@ __global__ __launch_bounds__(256) void act_absmax_kernel(const void* __restrict_
 
 namespace svdq {
 
-svdq_status launch_act_quant_int4(const void* X, svdq_dtype dt, int64_t M, int64_t K,
-                                  int rank, const float* smooth, const uint16_t* down,
-                                  uint8_t* codes, float* scales, uint16_t* LR,
-                                  hipStream_t s) {
+svdq_status launch_act_quant_int4(const void* X, svdq_dtype dt, bool gelu, int64_t M,
+                                  int64_t K, int rank, const float* smooth,
+                                  const uint16_t* down, uint8_t* codes, float* scales,
+                                  uint16_t* LR, hipStream_t s) {
   if (M == 0) return SVDQ_OK;
-  return RankDispatch<Int4Launch, 0>::run(rank / 16, dt == SVDQ_F32, X, int(M), int(K),
+  const int xin = dt == SVDQ_F32 ? 1 : (gelu ? 2 : 0);
+  return RankDispatch<Int4Launch, 0>::run(rank / 16, xin, X, int(M), int(K),
                                           smooth, down, codes, scales, LR, s);
 }
 
-svdq_status launch_act_quant_nvfp4(const void* X, svdq_dtype dt, int64_t M, int64_t K,
-                                   int rank, const float* smooth, const uint16_t* down,
-                                   const float* ts_x, uint8_t* codes, uint8_t* scales,
-                                   uint16_t* LR, hipStream_t s) {
+svdq_status launch_act_quant_nvfp4(const void* X, svdq_dtype dt, bool gelu, int64_t M,
+                                   int64_t K, int rank, const float* smooth,
+                                   const uint16_t* down, const float* ts_x, uint8_t* codes,
+                                   uint8_t* scales, uint16_t* LR, hipStream_t s) {
   if (M == 0) return SVDQ_OK;
-  return RankDispatch<Fp4Launch, 0>::run(rank / 16, dt == SVDQ_F32, X, int(M), int(K),
+  const int xin = dt == SVDQ_F32 ? 1 : (gelu ? 2 : 0);
+  return RankDispatch<Fp4Launch, 0>::run(rank / 16, xin, X, int(M), int(K),
                                          smooth, down, ts_x, codes, scales, LR, s);
 }
 

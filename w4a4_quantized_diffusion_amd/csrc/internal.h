@@ -32,14 +32,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ---------------------------------------------------------------- launches
 svdq_status launch_act_absmax(const void* X, svdq_dtype dt, int64_t M, int64_t K,
                               float* amax, hipStream_t s);
-svdq_status launch_act_quant_int4(const void* X, svdq_dtype dt, int64_t M, int64_t K,
-                                  int rank, const float* smooth, const uint16_t* down,
-                                  uint8_t* codes, float* scales, uint16_t* LR,
-                                  hipStream_t s);
-svdq_status launch_act_quant_nvfp4(const void* X, svdq_dtype dt, int64_t M, int64_t K,
-                                   int rank, const float* smooth, const uint16_t* down,
-                                   const float* ts_x, uint8_t* codes, uint8_t* scales,
-                                   uint16_t* LR, hipStream_t s);
+// gelu: X (bf16) goes through GELU first, as the MLP down-projection's input
+svdq_status launch_act_quant_int4(const void* X, svdq_dtype dt, bool gelu, int64_t M,
+                                  int64_t K, int rank, const float* smooth,
+                                  const uint16_t* down, uint8_t* codes, float* scales,
+                                  uint16_t* LR, hipStream_t s);
+svdq_status launch_act_quant_nvfp4(const void* X, svdq_dtype dt, bool gelu, int64_t M,
+                                   int64_t K, int rank, const float* smooth,
+                                   const uint16_t* down, const float* ts_x, uint8_t* codes,
+                                   uint8_t* scales, uint16_t* LR, hipStream_t s);
 svdq_status launch_gemm_int4(const uint8_t* A, const float* sA, const uint16_t* LR,
                              int64_t M, int64_t K, int64_t N, int rank,
                              const uint8_t* W, const float* sW, const uint16_t* up,

@@ -147,12 +147,18 @@ svdq_status svdq_quantize_weights(const float* W, int64_t N, int64_t K, const fl
                                      residual, stream);
 }
 
-svdq_status svdq_act_quantize(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
-                              int32_t rank, svdq_precision prec, const float* smooth,
-                              const uint16_t* lora_down, const float* x_tensor_scale,
-                              uint8_t* codes, void* scales, uint16_t* LR, hipStream_t stream) {
-  svdq::clear_error();
+}  // extern "C"
+
+namespace {
+
+// the activation step, with or without GELU applied to X first
+svdq_status act_quantize(const void* X, svdq_dtype x_dtype, bool gelu, int64_t M, int64_t K,
+                         int32_t rank, svdq_precision prec, const float* smooth,
+                         const uint16_t* lora_down, const float* x_tensor_scale,
+                         uint8_t* codes, void* scales, uint16_t* LR, hipStream_t stream) {
   TRY(check_dtype(x_dtype, "x_dtype"));
+  if (gelu && x_dtype != SVDQ_BF16)
+    return fail(SVDQ_ERR_UNSUPPORTED, "the GELU input form takes bf16 activations");
   TRY(check_prec(prec));
   TRY(check_mkr(M, K, rank));
   if (M == 0) return SVDQ_OK;
@@ -166,12 +172,35 @@ svdq_status svdq_act_quantize(const void* X, svdq_dtype x_dtype, int64_t M, int6
   }
   if (prec == SVDQ_NVFP4) {
     TRY(check_ptr(x_tensor_scale, "x_tensor_scale", 4));
-    return svdq::launch_act_quant_nvfp4(X, x_dtype, M, K, rank, smooth, lora_down,
+    return svdq::launch_act_quant_nvfp4(X, x_dtype, gelu, M, K, rank, smooth, lora_down,
                                         x_tensor_scale, codes, static_cast<uint8_t*>(scales),
                                         LR, stream);
   }
-  return svdq::launch_act_quant_int4(X, x_dtype, M, K, rank, smooth, lora_down, codes,
+  return svdq::launch_act_quant_int4(X, x_dtype, gelu, M, K, rank, smooth, lora_down, codes,
                                      static_cast<float*>(scales), LR, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_act_quantize(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                              int32_t rank, svdq_precision prec, const float* smooth,
+                              const uint16_t* lora_down, const float* x_tensor_scale,
+                              uint8_t* codes, void* scales, uint16_t* LR, hipStream_t stream) {
+  svdq::clear_error();
+  return act_quantize(X, x_dtype, false, M, K, rank, prec, smooth, lora_down, x_tensor_scale,
+                      codes, scales, LR, stream);
+}
+
+svdq_status svdq_act_quantize_gelu(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                                   int32_t rank, svdq_precision prec, const float* smooth,
+                                   const uint16_t* lora_down, const float* x_tensor_scale,
+                                   uint8_t* codes, void* scales, uint16_t* LR,
+                                   hipStream_t stream) {
+  svdq::clear_error();
+  return act_quantize(X, x_dtype, true, M, K, rank, prec, smooth, lora_down, x_tensor_scale,
+                      codes, scales, LR, stream);
 }
 
 svdq_status svdq_gemm_w4a4(const uint8_t* codes, const void* scales, const uint16_t* LR,
@@ -212,15 +241,20 @@ svdq_status svdq_gemm_w4a4(const uint8_t* codes, const void* scales, const uint1
                                 bias_dtype, Y, y_dtype, stream);
 }
 
-svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K, int64_t N,
-                             int32_t rank, svdq_precision prec, const float* smooth,
-                             const uint16_t* lora_down, const uint16_t* lora_up,
-                             const uint8_t* wcodes, const void* wscales,
-                             const float* w_tensor_scale, const float* x_tensor_scale,
-                             const void* bias, void* Y, svdq_dtype y_dtype, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-  svdq::clear_error();
+}  // extern "C"
+
+namespace {
+
+svdq_status linear_w4a4(const void* X, svdq_dtype x_dtype, bool gelu, int64_t M, int64_t K,
+                        int64_t N, int32_t rank, svdq_precision prec, const float* smooth,
+                        const uint16_t* lora_down, const uint16_t* lora_up,
+                        const uint8_t* wcodes, const void* wscales,
+                        const float* w_tensor_scale, const float* x_tensor_scale,
+                        const void* bias, void* Y, svdq_dtype y_dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
   TRY(check_dtype(x_dtype, "x_dtype"));
+  if (gelu && x_dtype != SVDQ_BF16)
+    return fail(SVDQ_ERR_UNSUPPORTED, "the GELU input form takes bf16 activations");
   TRY(check_prec(prec));
   TRY(check_mkr(M, K, rank));
   if (N <= 0 || N > MAX_DIM || N % 16 != 0)
@@ -242,13 +276,44 @@ svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64
       return fail(SVDQ_ERR_INVALID_ARG, "X, Y and workspace must not overlap");
   }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  TRY(svdq_act_quantize(X, x_dtype, M, K, rank, prec, smooth, lora_down, x_tensor_scale,
-                        ws + l.codes, ws + l.scales,
-                        rank > 0 ? reinterpret_cast<uint16_t*>(ws + l.lr) : nullptr, stream));
+  TRY(act_quantize(X, x_dtype, gelu, M, K, rank, prec, smooth, lora_down, x_tensor_scale,
+                   ws + l.codes, ws + l.scales,
+                   rank > 0 ? reinterpret_cast<uint16_t*>(ws + l.lr) : nullptr, stream));
   return svdq_gemm_w4a4(ws + l.codes, ws + l.scales,
                         rank > 0 ? reinterpret_cast<const uint16_t*>(ws + l.lr) : nullptr, M, K,
                         N, rank, prec, wcodes, wscales, lora_up, w_tensor_scale,
                         x_tensor_scale, bias, x_dtype, Y, y_dtype, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K, int64_t N,
+                             int32_t rank, svdq_precision prec, const float* smooth,
+                             const uint16_t* lora_down, const uint16_t* lora_up,
+                             const uint8_t* wcodes, const void* wscales,
+                             const float* w_tensor_scale, const float* x_tensor_scale,
+                             const void* bias, void* Y, svdq_dtype y_dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  svdq::clear_error();
+  return linear_w4a4(X, x_dtype, false, M, K, N, rank, prec, smooth, lora_down, lora_up, wcodes,
+                     wscales, w_tensor_scale, x_tensor_scale, bias, Y, y_dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                                  int64_t N, int32_t rank, svdq_precision prec,
+                                  const float* smooth, const uint16_t* lora_down,
+                                  const uint16_t* lora_up, const uint8_t* wcodes,
+                                  const void* wscales, const float* w_tensor_scale,
+                                  const float* x_tensor_scale, const void* bias, void* Y,
+                                  svdq_dtype y_dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  svdq::clear_error();
+  return linear_w4a4(X, x_dtype, true, M, K, N, rank, prec, smooth, lora_down, lora_up, wcodes,
+                     wscales, w_tensor_scale, x_tensor_scale, bias, Y, y_dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 svdq_status awq_quantize_weights(const float* W, int64_t N, int64_t K, int32_t group, uint8_t* q,

@@ -36,11 +36,16 @@ _SIG = {
                                               _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "svdq_act_quantize": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I32, ctypes.c_int,
                                           _P, _P, _P, _P, _P, _P, _P]),
+    "svdq_act_quantize_gelu": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I32, ctypes.c_int,
+                                               _P, _P, _P, _P, _P, _P, _P]),
     "svdq_gemm_w4a4": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, ctypes.c_int, _P, _P,
                                        _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P]),
     "svdq_linear_w4a4": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I32, ctypes.c_int,
                                          _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
                                          ctypes.c_size_t, _P]),
+    "svdq_linear_w4a4_gelu": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I32,
+                                              ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "awq_quantize_weights": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "awq_linear_w4a16": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P,
                                          ctypes.c_int, _P]),
@@ -154,7 +159,7 @@ def svdq_quantize_weights(W, act_amax, rank, prec="int4", lowrank=None, residual
     return out
 
 
-def svdq_act_quantize(X, layer, codes=None, scales=None, LR=None):
+def svdq_act_quantize(X, layer, codes=None, scales=None, LR=None, _entry="svdq_act_quantize"):
     """The activation kernel alone: returns (codes, scales, LR).  Codes are
     chunk-major [K/64][M][32]; scales [K/64][M] f32 (INT4) or [K/64][M][4]
     E4M3 bytes (NVFP4)."""
@@ -167,11 +172,17 @@ def svdq_act_quantize(X, layer, codes=None, scales=None, LR=None):
                   else _empty((K // 64, M, 4), torch.uint8, dev))
     if LR is None and rank:
         LR = _empty((M, rank), torch.int16, dev)
-    _check(lib().svdq_act_quantize(
+    _check(getattr(lib(), _entry)(
         _p(X), _DT[X.dtype], M, K, rank, pr, _p(layer["smooth"]),
         _p(layer["lora_down"]) if rank else None, _p(layer["x_tensor_scale"]),
         _p(codes), _p(scales), _p(LR) if rank else None, _stream()))
     return codes, scales, LR
+
+
+def svdq_act_quantize_gelu(X, layer, codes=None, scales=None, LR=None):
+    """svdq_act_quantize on bf16(GELU(X)) (X bf16): the MLP down-projection's
+    activation step with the GELU fused in."""
+    return svdq_act_quantize(X, layer, codes, scales, LR, _entry="svdq_act_quantize_gelu")
 
 
 def svdq_gemm_w4a4(codes, scales, LR, layer, bias=None, y_dtype=torch.float32, Y=None):
@@ -188,7 +199,8 @@ def svdq_gemm_w4a4(codes, scales, LR, layer, bias=None, y_dtype=torch.float32, Y
     return Y
 
 
-def svdq_linear_w4a4(X, layer, bias=None, y_dtype=torch.float32, workspace=None, Y=None):
+def svdq_linear_w4a4(X, layer, bias=None, y_dtype=torch.float32, workspace=None, Y=None,
+                     _entry="svdq_linear_w4a4"):
     """The whole layer.  bias must have X's dtype.  Returns Y [M, N]."""
     M, K = X.shape
     N, rank, pr = layer["N"], layer["rank"], layer["prec"]
@@ -197,13 +209,19 @@ def svdq_linear_w4a4(X, layer, bias=None, y_dtype=torch.float32, workspace=None,
     need = svdq_workspace_bytes(M, K, rank, pr)
     if workspace is None:
         workspace = _empty((max(need, 256),), torch.uint8, X.device)
-    _check(lib().svdq_linear_w4a4(
+    _check(getattr(lib(), _entry)(
         _p(X), _DT[X.dtype], M, K, N, rank, pr, _p(layer["smooth"]),
         _p(layer["lora_down"]) if rank else None, _p(layer["lora_up"]) if rank else None,
         _p(layer["wcodes"]), _p(layer["wscales"]), _p(layer["w_tensor_scale"]),
         _p(layer["x_tensor_scale"]), _p(bias), _p(Y), _DT[Y.dtype], _p(workspace),
         workspace.numel(), _stream()))
     return Y
+
+
+def svdq_linear_w4a4_gelu(X, layer, bias=None, y_dtype=torch.float32, workspace=None, Y=None):
+    """The whole layer on bf16(GELU(X)) (X bf16): the MLP down-projection with
+    the GELU fused into the activation pass."""
+    return svdq_linear_w4a4(X, layer, bias, y_dtype, workspace, Y, _entry="svdq_linear_w4a4_gelu")
 
 
 def workspace_views(workspace, M, K, rank, prec="int4"):
