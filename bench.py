@@ -238,7 +238,28 @@ def other_paths(steps):
         "act_quant_gelu_frac_hbm": round(act_bytes / t_act_g / 1e9 / PEAK_HBM_GBS, 4),
         "unfused_gelu_pass_bytes": 2 * M * K * 2,
     }
-    del x, lay, y, ws, codes, scales, lr
+    # the same layer with a rank-16 LoRA adapter folded into its 16-bit branch
+    RL = 16
+    a, b = synth.lora_adapter(N, K, RL, 0)
+    at = torch.from_numpy(a).to(dev).to(torch.bfloat16)
+    bt = torch.from_numpy(b).to(dev).to(torch.bfloat16)
+    lay_l = svdq.svdq_fold_lora(lay, at, bt, 1.0)
+    ws_l = torch.empty(svdq.svdq_workspace_bytes(M, K, lay_l["rank"]), dtype=torch.uint8,
+                       device=dev)
+    t_fold = time_loop(lambda i: svdq.svdq_fold_lora(lay, at, bt, 1.0), 20, warmup=5)
+    t_lin_l = time_loop(lambda i: svdq.svdq_linear_w4a4(x, lay_l, workspace=ws_l, Y=y), steps,
+                        warmup=steps)
+    fold_bytes = 2 * (R * K + N * R + RL * K + N * RL) + 2 * lay_l["rank"] * (K + N)
+    res["int4_lora_folded"] = {
+        "workload": f"INT4 g64, rank {R} + LoRA rank {RL} folded (rank {lay_l['rank']}), "
+                    "M 4608 x K 12288 -> N 3072",
+        "timing": "back-to-back loop averages",
+        "linear_us": round(t_lin_l * 1e6, 2),
+        "linear_without_lora_us": round(t_lin_p * 1e6, 2),
+        "fold_us": round(t_fold * 1e6, 2),
+        "fold_GB/s": round(fold_bytes / t_fold / 1e9, 1),
+    }
+    del x, lay, y, ws, codes, scales, lr, lay_l, ws_l, at, bt
     torch.cuda.empty_cache()
 
     # AWQ W4A16

@@ -212,6 +212,29 @@ svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, 
                                   void* Y, svdq_dtype y_dtype, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/* LoRA folded into the 16-bit low-rank branch (offline, once per adapter).
+ * A LoRA adapter adds scale * B (A x) to the layer's output; LoRA loading
+ * keeps working on the quantized models ("Hugging Face Integrates Nunchaku
+ * Lite for Native 4-bit Diffusion Inference", Broader Ecosystem Impact).
+ * The branch already reads raw X in 16 bits, so the adapter is a longer
+ * rank:
+ *   lora_down_out [r_new, K] = rows of lora_down, then rows of A, then zeros
+ *   lora_up_out   [N, r_new] = columns of lora_up, then columns of
+ *                              bf16(fl32(scale * B)) (RNE), then zeros
+ *   r_new = round_up(rank + r_lora, 16), returned in *rank_out (HOST int32).
+ * The layer then runs with rank r_new and the new factors; the zero padding
+ * adds exact zeros.  Inputs, DEVICE bf16 bit patterns, row-major: lora_down
+ * [rank, K], lora_up [N, rank] (both may be NULL when rank == 0), A
+ * [r_lora, K], B [N, r_lora].  Outputs are caller-owned DEVICE buffers of the
+ * sizes above; they may not overlap the inputs or each other.
+ * rank % 16 == 0, 1 <= r_lora, r_new <= 256, K % 64 == 0, scale finite; else
+ * SVDQ_ERR_INVALID_ARG and nothing is written.  One kernel, asynchronous on
+ * `stream`. */
+svdq_status svdq_fold_lora(const uint16_t* lora_down, const uint16_t* lora_up, int64_t N,
+                           int64_t K, int32_t rank, const uint16_t* A, const uint16_t* B,
+                           int32_t r_lora, float scale, uint16_t* lora_down_out,
+                           uint16_t* lora_up_out, int32_t* rank_out, hipStream_t stream);
+
 /* Offline AWQ W4A16 quantization (asymmetric INT4, the awq_w4a16 row of the
  * "Hardware-Support" table).  Per output row and group of `group` along K:
  *   mn = min(min w, 0), mx = max(max w, 0), s = bf16(fl32(fl32(mx - mn) / 15))

@@ -291,3 +291,31 @@ def gelu_input(x):
     evaluation, then bf16).  Returns float32 values that are bf16 values."""
     return bf16(gelu_tanh(x)).astype(np.float32)
 
+
+
+# ---------------------------------------------------------------- LoRA fold
+
+def fold_lora(lora_down, lora_up, a, b, scale=1.0):
+    """A LoRA adapter scale * B A (A [r_lora, K], B [N, r_lora], bf16 values)
+    folded into the 16-bit low-rank branch by rank concatenation (LoRA loading
+    keeps working on the quantized models: "Hugging Face Integrates Nunchaku
+    Lite for Native 4-bit Diffusion Inference", Broader Ecosystem Impact).
+    The branch reads raw X, as the adapter does, so
+
+      lora_down' = [lora_down ; A ; 0],  lora_up' = [lora_up | bf16(fl32(scale B)) | 0]
+
+    with the rank padded by zero rows / columns to a multiple of 16.  Returns
+    (lora_down', lora_up', r_new) as float64 values."""
+    a = np.asarray(a, dtype=F64)
+    b = np.asarray(b, dtype=F64)
+    r_lora, k = a.shape
+    n = b.shape[0]
+    down = np.zeros((0, k)) if lora_down is None else np.asarray(lora_down, dtype=F64)
+    up = np.zeros((n, 0)) if lora_up is None else np.asarray(lora_up, dtype=F64)
+    rank = down.shape[0]
+    r_new = -(-(rank + r_lora) // 16) * 16
+    pad = r_new - rank - r_lora
+    bs = bf16(fl32(np.float32(scale) * b.astype(np.float32).astype(F64)))
+    down2 = np.concatenate([down, a, np.zeros((pad, k))], axis=0)
+    up2 = np.concatenate([up, bs, np.zeros((n, pad))], axis=1)
+    return down2, up2, r_new

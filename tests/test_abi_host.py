@@ -156,3 +156,34 @@ def test_gelu_forms_take_bf16_only(lib):
     assert st == INVALID and "K must" in svdq.svdq_last_error()
     assert lib.svdq_act_quantize_gelu(None, 1, 0, 128, 16, 0, None, None, None, None, None, None,
                                       None) == 0
+
+
+def test_fold_lora_validation(lib):
+    p = ctypes.c_void_p
+    r = ctypes.c_int32(-1)
+    f = lib.svdq_fold_lora
+    # rank not a multiple of 16, rank + r_lora past 256, r_lora 0, K not a multiple of 64
+    assert f(p(0x1000), p(0x2000), 64, 128, 8, p(0x3000), p(0x4000), 4, 1.0, p(0x10000),
+             p(0x20000), ctypes.byref(r), None) == INVALID
+    assert "rank" in svdq.svdq_last_error()
+    assert f(p(0x1000), p(0x2000), 64, 128, 240, p(0x3000), p(0x4000), 17, 1.0, p(0x10000),
+             p(0x20000), ctypes.byref(r), None) == INVALID
+    assert "256" in svdq.svdq_last_error()
+    assert f(None, None, 64, 128, 0, p(0x3000), p(0x4000), 0, 1.0, p(0x10000), p(0x20000),
+             ctypes.byref(r), None) == INVALID
+    assert f(None, None, 64, 100, 0, p(0x3000), p(0x4000), 4, 1.0, p(0x10000), p(0x20000),
+             ctypes.byref(r), None) == INVALID
+    assert f(None, None, 64, 128, 0, p(0x3000), p(0x4000), 4, float("nan"), p(0x10000),
+             p(0x20000), ctypes.byref(r), None) == INVALID
+    assert "finite" in svdq.svdq_last_error()
+    # NULL adapter, NULL rank_out, and outputs overlapping an input
+    assert f(None, None, 64, 128, 0, None, p(0x4000), 4, 1.0, p(0x10000), p(0x20000),
+             ctypes.byref(r), None) == INVALID
+    assert "NULL" in svdq.svdq_last_error()
+    assert f(None, None, 64, 128, 0, p(0x3000), p(0x4000), 4, 1.0, p(0x10000), p(0x20000),
+             None, None) == INVALID
+    # A [4, 128] bf16 = 1 KiB at 0x3000 overlaps lora_down_out at 0x3200
+    assert f(None, None, 64, 128, 0, p(0x3000), p(0x40000), 4, 1.0, p(0x3200), p(0x80000),
+             ctypes.byref(r), None) == INVALID
+    assert "overlap" in svdq.svdq_last_error()
+    assert r.value == -1

@@ -58,6 +58,10 @@ svdq_status quantize_weights_impl(const float* W, int64_t N, int64_t K,
                                   uint16_t* up, uint8_t* wcodes, void* wscales,
                                   float* ts_w, float* ts_x, float* residual,
                                   hipStream_t s);
+svdq_status launch_fold_lora(const uint16_t* down, const uint16_t* up, int64_t N, int64_t K,
+                             int rank, const uint16_t* A, const uint16_t* B, int r_lora,
+                             float scale, int r_new, uint16_t* down_out, uint16_t* up_out,
+                             hipStream_t s);
 svdq_status launch_awq_quant(const float* W, int64_t N, int64_t K, uint8_t* q,
                              uint16_t* scales, uint16_t* zeros, hipStream_t s);
 svdq_status launch_awq_linear(const uint16_t* X, int64_t M, int64_t K, int64_t N,

@@ -316,6 +316,51 @@ svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, 
                      workspace_bytes, stream);
 }
 
+svdq_status svdq_fold_lora(const uint16_t* lora_down, const uint16_t* lora_up, int64_t N,
+                           int64_t K, int32_t rank, const uint16_t* A, const uint16_t* B,
+                           int32_t r_lora, float scale, uint16_t* lora_down_out,
+                           uint16_t* lora_up_out, int32_t* rank_out, hipStream_t stream) {
+  svdq::clear_error();
+  if (N <= 0 || N > MAX_DIM || K <= 0 || K > MAX_DIM || K % 64 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "N > 0 and K a positive multiple of 64 required");
+  if (rank < 0 || rank % 16 != 0 || rank > 256)
+    return fail(SVDQ_ERR_INVALID_ARG, "rank must be a multiple of 16 in [0, 256]");
+  if (r_lora <= 0 || r_lora > 256) return fail(SVDQ_ERR_INVALID_ARG, "r_lora must be in [1, 256]");
+  const int32_t r_new = (rank + r_lora + 15) / 16 * 16;
+  if (r_new > 256) return fail(SVDQ_ERR_INVALID_ARG, "rank + r_lora must stay at most 256");
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+    return fail(SVDQ_ERR_INVALID_ARG, "scale must be finite");
+  if (!rank_out) return fail(SVDQ_ERR_INVALID_ARG, "rank_out is NULL");
+  if (rank > 0) {
+    TRY(check_ptr(lora_down, "lora_down", 2));
+    TRY(check_ptr(lora_up, "lora_up", 2));
+  }
+  TRY(check_ptr(A, "A", 2));
+  TRY(check_ptr(B, "B", 2));
+  TRY(check_ptr(lora_down_out, "lora_down_out", 2));
+  TRY(check_ptr(lora_up_out, "lora_up_out", 2));
+  {
+    // the outputs may not overlap any input or each other
+    const size_t e = sizeof(uint16_t);
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(lora_down_out), d1 = d0 + size_t(r_new) * K * e;
+    const uintptr_t u0 = reinterpret_cast<uintptr_t>(lora_up_out), u1 = u0 + size_t(N) * r_new * e;
+    const struct { const void* p; size_t b; } in[4] = {
+        {lora_down, size_t(rank) * K * e}, {lora_up, size_t(N) * rank * e},
+        {A, size_t(r_lora) * K * e}, {B, size_t(N) * r_lora * e}};
+    bool bad = d0 < u1 && u0 < d1;
+    for (const auto& r : in) {
+      if (!r.p || r.b == 0) continue;
+      const uintptr_t p0 = reinterpret_cast<uintptr_t>(r.p), p1 = p0 + r.b;
+      bad = bad || (p0 < d1 && d0 < p1) || (p0 < u1 && u0 < p1);
+    }
+    if (bad) return fail(SVDQ_ERR_INVALID_ARG, "the outputs must not overlap the inputs or each other");
+  }
+  TRY(svdq::launch_fold_lora(lora_down, lora_up, N, K, rank, A, B, r_lora, scale, r_new,
+                             lora_down_out, lora_up_out, stream));
+  *rank_out = r_new;
+  return SVDQ_OK;
+}
+
 svdq_status awq_quantize_weights(const float* W, int64_t N, int64_t K, int32_t group, uint8_t* q,
                                  uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
   svdq::clear_error();

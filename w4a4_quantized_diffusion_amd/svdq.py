@@ -46,6 +46,8 @@ _SIG = {
     "svdq_linear_w4a4_gelu": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I32,
                                               ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "svdq_fold_lora": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P, _I32, ctypes.c_float,
+                                       _P, _P, _P, _P]),
     "awq_quantize_weights": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "awq_linear_w4a16": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P,
                                          ctypes.c_int, _P]),
@@ -204,6 +206,8 @@ def svdq_linear_w4a4(X, layer, bias=None, y_dtype=torch.float32, workspace=None,
     """The whole layer.  bias must have X's dtype.  Returns Y [M, N]."""
     M, K = X.shape
     N, rank, pr = layer["N"], layer["rank"], layer["prec"]
+    if bias is not None and bias.dtype != X.dtype:
+        raise ValueError("bias must have X's dtype")
     if Y is None:
         Y = _empty((M, N), y_dtype, X.device)
     need = svdq_workspace_bytes(M, K, rank, pr)
@@ -222,6 +226,35 @@ def svdq_linear_w4a4_gelu(X, layer, bias=None, y_dtype=torch.float32, workspace=
     """The whole layer on bf16(GELU(X)) (X bf16): the MLP down-projection with
     the GELU fused into the activation pass."""
     return svdq_linear_w4a4(X, layer, bias, y_dtype, workspace, Y, _entry="svdq_linear_w4a4_gelu")
+
+
+def _bf16_bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def svdq_fold_lora(layer, A, B, scale=1.0):
+    """A layer dict whose low-rank branch also carries the LoRA adapter
+    scale * B A (A [r_lora, K], B [N, r_lora], bf16 or their int16 bit
+    patterns): rank becomes round_up(rank + r_lora, 16), lora_down / lora_up
+    are new tensors, every other entry is shared with `layer`."""
+    N, K, rank = layer["N"], layer["K"], layer["rank"]
+    A, B = _bf16_bits(A), _bf16_bits(B)
+    r_lora = A.shape[0]
+    if A.dim() != 2 or A.shape[1] != K or B.dim() != 2 or tuple(B.shape) != (N, r_lora):
+        raise ValueError("A must be [r_lora, K] and B [N, r_lora]")
+    r_new = (rank + r_lora + 15) // 16 * 16
+    dev = A.device
+    down = _empty((r_new, K), torch.int16, dev)
+    up = _empty((N, r_new), torch.int16, dev)
+    got = ctypes.c_int32()
+    _check(lib().svdq_fold_lora(
+        _p(layer["lora_down"]) if rank else None, _p(layer["lora_up"]) if rank else None,
+        N, K, rank, _p(A), _p(B), r_lora, float(scale), _p(down), _p(up),
+        ctypes.byref(got), _stream()))
+    assert got.value == r_new
+    out = dict(layer)
+    out.update(rank=r_new, lora_down=down, lora_up=up)
+    return out
 
 
 def workspace_views(workspace, M, K, rank, prec="int4"):

@@ -24,7 +24,7 @@ Workloads (ids are fixed; shapes follow the diffusion-transformer layers):
 
 import numpy as np
 
-WORKLOADS = {"small": 0, "attn": 1, "mlp": 2, "mlp_fp4": 3, "awq": 4, "flagship": 5}
+WORKLOADS = {"small": 0, "attn": 1, "mlp": 2, "mlp_fp4": 3, "awq": 4, "flagship": 5, "lora": 6}
 
 
 def rng(seed, workload, tensor):
@@ -118,3 +118,11 @@ def random_int4_layer(n, k, rank, seed=0, workload="flagship"):
     down = to_bf16_bits(round_bf16((g.standard_normal((rank, k)) * 0.05).astype(np.float32)))
     up = to_bf16_bits(round_bf16((g.standard_normal((n, rank)) * 0.02).astype(np.float32)))
     return dict(wcodes=wcodes, sW=sw, smooth=smooth, lora_down_bits=down, lora_up_bits=up)
+
+
+def lora_adapter(n, k, r_lora, seed=0, std=0.05):
+    """A LoRA adapter's factors A [r_lora, K] and B [N, r_lora]: Gaussian
+    entries of the given std, rounded to bf16 values (float32)."""
+    w = WORKLOADS["lora"]
+    return (round_bf16(gaussian((r_lora, k), std, seed, w, 1)),
+            round_bf16(gaussian((n, r_lora), std, seed, w, 2)))
