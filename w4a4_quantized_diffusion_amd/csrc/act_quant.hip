@@ -53,19 +53,23 @@ struct XRaw {
 // per lane; instead lane l loads the 16 bytes at rank (l / 8) + 8 i, column
 // chunk l % 8 (eight lanes cover one rank's 128 contiguous bytes), and the
 // wave passes them through a private LDS tile into the MFMA layout.
+// The 16-row kernels prefetch up to rank 32 (beyond, the prefetch registers
+// push them into scratch); the 8-row kernel, with half the X registers, up
+// to rank 64.
 constexpr int RB_PREFETCH = 2;
-template <int RB>
+constexpr int RB_PREFETCH8 = 4;
+template <int RB, bool PRE>
 struct DownRaw {
-  uint4 v[RB > 0 && RB <= RB_PREFETCH ? 2 * RB : 1];
+  uint4 v[RB > 0 && PRE ? 2 * RB : 1];
 };
 // the tile: rank rows of 8 chunks of 16 bytes, padded to 144 bytes so that
 // the 16 lanes of an MFMA operand read (16 ranks, one chunk) hit distinct banks
 constexpr int DOWN_ROW = 144;
 
-template <int RB>
+template <int RB, bool PRE>
 __device__ __forceinline__ void load_down(const uint16_t* __restrict__ down, int K, int lane,
-                                          int kg, DownRaw<RB>& d) {
-  if constexpr (RB > 0 && RB <= RB_PREFETCH) {
+                                          int kg, DownRaw<RB, PRE>& d) {
+  if constexpr (RB > 0 && PRE) {
 #pragma unroll
     for (int i = 0; i < 2 * RB; ++i) {
       const uint16_t* p = down + int64_t((lane >> 3) + 8 * i) * K + kg + 8 * (lane & 7);
@@ -74,9 +78,9 @@ __device__ __forceinline__ void load_down(const uint16_t* __restrict__ down, int
   }
 }
 
-template <int RB>
-__device__ __forceinline__ void stage_down(uint8_t* tile, int lane, const DownRaw<RB>& d) {
-  if constexpr (RB > 0 && RB <= RB_PREFETCH) {
+template <int RB, bool PRE>
+__device__ __forceinline__ void stage_down(uint8_t* tile, int lane, const DownRaw<RB, PRE>& d) {
+  if constexpr (RB > 0 && PRE) {
 #pragma unroll
     for (int i = 0; i < 2 * RB; ++i)
       *reinterpret_cast<v4i*>(tile + ((lane >> 3) + 8 * i) * DOWN_ROW + (lane & 7) * 16) =
@@ -290,7 +294,7 @@ __device__ __forceinline__ void lr_mfma(v4f (&acc)[RB > 0 ? RB : 1], const uint3
 template <int RB>
 __device__ __forceinline__ void lr_mfma_pre(v4f (&acc)[RB > 0 ? RB : 1], const uint32_t (&xb)[4],
                                             const uint8_t* tile, int lane, int h) {
-  if constexpr (RB > 0 && RB <= RB_PREFETCH) {
+  if constexpr (RB > 0) {
     v4i ai = {int(xb[0]), int(xb[1]), int(xb[2]), int(xb[3])};
     v8bf a = __builtin_bit_cast(v8bf, ai);
 #pragma unroll
@@ -335,6 +339,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     float* __restrict__ scales, uint16_t* __restrict__ LR) {
   extern __shared__ float red[];
   constexpr bool XF32 = XIN == 1;
+  constexpr bool PRE = RB <= RB_PREFETCH;   // lora_down prefetched with X
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
   const int T = (G - wave + WAVES - 1) / WAVES;
   const int64_t xrow = ok ? row : M - 1;
   XRaw<XF32> ring[DEPTH];
-  DownRaw<RB> dring[DEPTH];
+  DownRaw<RB, PRE> dring[DEPTH];
   SmoothRaw sring[DEPTH];
   // every slot is always (re)loaded, past the last group with the last
   // group's data, so that the ring keeps fixed registers and its loads stay
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     const int gg = tc >= 0 ? wave + WAVES * tc : 0;
     load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
     load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
-    load_down<RB>(down, K, lane, gg * 64, dring[sl_]);
+    load_down<RB, PRE>(down, K, lane, gg * 64, dring[sl_]);
   };
 #pragma unroll
   for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
@@ -437,8 +442,8 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
       cp[4 + q] = w1;
       if (q == 0) scales[int64_t(g) * M + row] = s;
     }
-    if constexpr (RB <= RB_PREFETCH) {
-      stage_down<RB>(dtile, lane, dring[sl]);
+    if constexpr (PRE) {
+      stage_down<RB, PRE>(dtile, lane, dring[sl]);
       lr_mfma_pre<RB>(acc, b0, dtile, lane, 0);
       lr_mfma_pre<RB>(acc, b1, dtile, lane, 1);
     } else {
@@ -461,6 +466,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ LR) {
   extern __shared__ float red[];
   constexpr bool XF32 = XIN == 1;
+  constexpr bool PRE = RB <= RB_PREFETCH;   // lora_down prefetched with X
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
   const int T = (G - wave + WAVES - 1) / WAVES;
   const int64_t xrow = ok ? row : M - 1;
   XRaw<XF32> ring[DEPTH];
-  DownRaw<RB> dring[DEPTH];
+  DownRaw<RB, PRE> dring[DEPTH];
   SmoothRaw sring[DEPTH];
   // every slot is always (re)loaded, past the last group with the last
   // group's data, so that the ring keeps fixed registers and its loads stay
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
     const int gg = tc >= 0 ? wave + WAVES * tc : 0;
     load_raw<XF32>(X, xrow * K + gg * 64 + 8 * q, ring[sl_]);
     load_smooth(smooth, gg * 64 + 8 * q, sring[sl_]);
-    load_down<RB>(down, K, lane, gg * 64, dring[sl_]);
+    load_down<RB, PRE>(down, K, lane, gg * 64, dring[sl_]);
   };
 #pragma unroll
   for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
@@ -568,8 +574,8 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
         sp[2 + (q >> 1)] = uint8_t(sb[1]);
       }
     }
-    if constexpr (RB <= RB_PREFETCH) {
-      stage_down<RB>(dtile, lane, dring[sl]);
+    if constexpr (PRE) {
+      stage_down<RB, PRE>(dtile, lane, dring[sl]);
       lr_mfma_pre<RB>(acc, b0, dtile, lane, 0);
       lr_mfma_pre<RB>(acc, b1, dtile, lane, 1);
     } else {
@@ -650,7 +656,8 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
     const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ down, const float* __restrict__ ts_x,
     uint8_t* __restrict__ codes, void* __restrict__ scales, uint16_t* __restrict__ LR) {
-  static_assert(RB <= RB_PREFETCH, "8-row workgroups take the prefetched lora_down path");
+  static_assert(RB <= RB_PREFETCH8, "8-row workgroups take the prefetched lora_down path");
+  constexpr bool PRE = true;
   extern __shared__ float red[];
   constexpr bool XF32 = XIN == 1;
   const int lane = threadIdx.x & 63;
@@ -683,14 +690,14 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
   const int T = (G - wave + WAVES - 1) / WAVES;
   const int64_t xrow = ok ? row : M - 1;
   XRaw8<XF32> ring[DEPTH];
-  DownRaw<RB> dring[DEPTH];
+  DownRaw<RB, PRE> dring[DEPTH];
   SmoothRaw8 sring[DEPTH];
   auto fetch = [&](int tt, int sl_) __attribute__((always_inline)) {
     const int tc = tt < T ? tt : T - 1;
     const int gg = tc >= 0 ? wave + WAVES * tc : 0;
     load_raw8<XF32>(X, xrow * K + gg * 64 + 8 * c, ring[sl_]);
     load_smooth8(smooth, gg * 64 + 8 * c, sring[sl_]);
-    load_down<RB>(down, K, lane, gg * 64, dring[sl_]);
+    load_down<RB, PRE>(down, K, lane, gg * 64, dring[sl_]);
   };
 #pragma unroll
   for (int sl = 0; sl < DEPTH; ++sl) fetch(sl, sl);
@@ -777,7 +784,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
       }
     }
     if constexpr (RB > 0) {
-      stage_down<RB>(dtile, lane, dring[sl]);
+      stage_down<RB, true>(dtile, lane, dring[sl]);
       const v4i ai = {int(b[0]), int(b[1]), int(b[2]), int(b[3])};
       const v8bf av = __builtin_bit_cast(v8bf, ai);
 #pragma unroll
@@ -844,9 +851,12 @@ int cu_count() {
 
 // Whether 8-row workgroups finish sooner than 16-row ones: with one
 // workgroup per CU, the time goes as (rounds of workgroups) x (rows each).
+// Ranks past the 16-row kernels' prefetch limit always take 8-row
+// workgroups, whose prefetched lora_down tiles beat the direct loads.
 bool use_rows8(int M, int RB) {
   const int cus = cu_count();
-  if (RB > RB_PREFETCH || cus <= 0) return false;
+  if (RB > RB_PREFETCH8 || cus <= 0) return false;
+  if (RB > RB_PREFETCH) return true;
   auto cost = [&](int rows) {
     const int64_t wgs = (int64_t(M) + rows - 1) / rows;
     return (wgs + cus - 1) / cus * rows;
@@ -854,11 +864,19 @@ bool use_rows8(int M, int RB) {
   return cost(ROWS8) < cost(ROWS);
 }
 
-// LR reduction buffer, then (small ranks) the waves' lora_down tiles
-constexpr size_t lds_bytes(int RB) {
+// LR reduction buffer, then (prefetching kernels) the waves' lora_down tiles
+constexpr size_t lds_bytes(int RB, bool pre) {
   return RB > 0 ? size_t(WAVES) * ROWS * RB * 16 * sizeof(float) +
-                      (RB <= RB_PREFETCH ? size_t(WAVES) * RB * 16 * DOWN_ROW : 0)
+                      (pre ? size_t(WAVES) * RB * 16 * DOWN_ROW : 0)
                 : 0;
+}
+
+// dynamic LDS beyond the default 64 KB needs the kernel's opt-in
+svdq_status lds_opt_in(const void* fn, size_t shm, const char* what) {
+  if (shm > 65536 &&
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
+    return svdq::fail(SVDQ_ERR_HIP, std::string(what) + ": shared memory size");
+  return SVDQ_OK;
 }
 
 template <int RB, int XIN>
@@ -866,23 +884,23 @@ struct Int4Launch {
   static svdq_status go(const void* X, int M, int K, const float* smooth,
                         const uint16_t* down, uint8_t* codes, float* scales, uint16_t* LR,
                         hipStream_t s) {
-    const size_t shm = lds_bytes(RB);
-    if constexpr (RB <= RB_PREFETCH) {
-      static_assert(lds_bytes(RB_PREFETCH) <= 65536, "no dynamic-LDS opt-in on this path");
+    if constexpr (RB <= RB_PREFETCH8) {
       if (use_rows8(M, RB)) {
-        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XIN, false>), dim3((M + ROWS8 - 1) / ROWS8),
-                           dim3(64 * WAVES), shm, s, X, M, K, smooth, down, nullptr, codes,
-                           static_cast<void*>(scales), LR);
+        const auto fn = act_quant_rows8_kernel<RB, XIN, false>;
+        const size_t shm = lds_bytes(RB, true);
+        const svdq_status st = lds_opt_in(reinterpret_cast<const void*>(fn), shm, "act_quant_int4");
+        if (st != SVDQ_OK) return st;
+        hipLaunchKernelGGL(fn, dim3((M + ROWS8 - 1) / ROWS8), dim3(64 * WAVES), shm, s, X, M, K,
+                           smooth, down, nullptr, codes, static_cast<void*>(scales), LR);
         return svdq::check_launch("act_quant_int4");
       }
     }
-    if (shm > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_int4_kernel<RB, XIN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
-      return svdq::fail(SVDQ_ERR_HIP, "act_quant_int4: shared memory size");
-    dim3 grid((M + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((act_quant_int4_kernel<RB, XIN>), grid, dim3(64 * WAVES), shm, s, X, M,
-                       K, smooth, down, codes, scales, LR);
+    const auto fn = act_quant_int4_kernel<RB, XIN>;
+    const size_t shm = lds_bytes(RB, RB <= RB_PREFETCH);
+    const svdq_status st = lds_opt_in(reinterpret_cast<const void*>(fn), shm, "act_quant_int4");
+    if (st != SVDQ_OK) return st;
+    hipLaunchKernelGGL(fn, dim3((M + ROWS - 1) / ROWS), dim3(64 * WAVES), shm, s, X, M, K, smooth,
+                       down, codes, scales, LR);
     return svdq::check_launch("act_quant_int4");
   }
 };
@@ -892,22 +910,23 @@ struct Fp4Launch {
   static svdq_status go(const void* X, int M, int K, const float* smooth,
                         const uint16_t* down, const float* ts_x, uint8_t* codes,
                         uint8_t* scales, uint16_t* LR, hipStream_t s) {
-    const size_t shm = lds_bytes(RB);
-    if constexpr (RB <= RB_PREFETCH) {
+    if constexpr (RB <= RB_PREFETCH8) {
       if (use_rows8(M, RB)) {
-        hipLaunchKernelGGL((act_quant_rows8_kernel<RB, XIN, true>), dim3((M + ROWS8 - 1) / ROWS8),
-                           dim3(64 * WAVES), shm, s, X, M, K, smooth, down, ts_x, codes,
-                           static_cast<void*>(scales), LR);
+        const auto fn = act_quant_rows8_kernel<RB, XIN, true>;
+        const size_t shm = lds_bytes(RB, true);
+        const svdq_status st = lds_opt_in(reinterpret_cast<const void*>(fn), shm, "act_quant_nvfp4");
+        if (st != SVDQ_OK) return st;
+        hipLaunchKernelGGL(fn, dim3((M + ROWS8 - 1) / ROWS8), dim3(64 * WAVES), shm, s, X, M, K,
+                           smooth, down, ts_x, codes, static_cast<void*>(scales), LR);
         return svdq::check_launch("act_quant_nvfp4");
       }
     }
-    if (shm > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(act_quant_nvfp4_kernel<RB, XIN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
-      return svdq::fail(SVDQ_ERR_HIP, "act_quant_nvfp4: shared memory size");
-    dim3 grid((M + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((act_quant_nvfp4_kernel<RB, XIN>), grid, dim3(64 * WAVES), shm, s, X,
-                       M, K, smooth, down, ts_x, codes, scales, LR);
+    const auto fn = act_quant_nvfp4_kernel<RB, XIN>;
+    const size_t shm = lds_bytes(RB, RB <= RB_PREFETCH);
+    const svdq_status st = lds_opt_in(reinterpret_cast<const void*>(fn), shm, "act_quant_nvfp4");
+    if (st != SVDQ_OK) return st;
+    hipLaunchKernelGGL(fn, dim3((M + ROWS - 1) / ROWS), dim3(64 * WAVES), shm, s, X, M, K, smooth,
+                       down, ts_x, codes, scales, LR);
     return svdq::check_launch("act_quant_nvfp4");
   }
 };
