@@ -598,7 +598,9 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_nvfp4_kernel(
 // l % 16 = row + 8 (chunk & 1) at k-slot chunk / 2: one MFMA with the
 // lora_down chunks 2j gives rows 0..7 the products of the even chunks, a
 // second with the chunks 2j + 1 gives rows 8..15 those of the odd ones, and
-// the row's partial LR is the sum of the two.
+// the row's partial LR is the sum of the two.  A workgroup has NW waves
+// (8, or 4 at large M with a low-rank branch: then two or three workgroups
+// share a CU); wave w takes the K-groups w, w + NW, ...
 constexpr int ROWS8 = 8;
 
 template <bool XF32>
@@ -651,8 +653,8 @@ __device__ __forceinline__ void load_smooth8(const float* __restrict__ smooth, i
 
 // FP4: NVFP4 codes and E4M3 block scales, else INT4 codes and f32 scales;
 // the same arithmetic as the 16-row kernels, per 8-element chunk
-template <int RB, int XIN, bool FP4>
-__global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
+template <int RB, int XIN, bool FP4, int NW>
+__global__ __launch_bounds__(64 * NW, NW >= 8 || RB > 2 ? 2 : 3) void act_quant_rows8_kernel(
     const void* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ down, const float* __restrict__ ts_x,
     uint8_t* __restrict__ codes, void* __restrict__ scales, uint16_t* __restrict__ LR) {
@@ -668,7 +670,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
   const bool ok = row < M;
   const int G = K / 64;
   // LR partials [wave][even / odd chunks][8 rows][R], then the lora_down tiles
-  uint8_t* const dtile = reinterpret_cast<uint8_t*>(red + WAVES * 16 * RB * 16) +
+  uint8_t* const dtile = reinterpret_cast<uint8_t*>(red + NW * 16 * RB * 16) +
                          wave * (RB * 16 * DOWN_ROW);
   float ts = 1.0f, d = 0.0f, rd_hi = 0.0f, rd_lo = 0.0f;
   bool d_ok = false;
@@ -687,14 +689,14 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
     acc_o[i] = v4f{0, 0, 0, 0};
   }
 
-  const int T = (G - wave + WAVES - 1) / WAVES;
+  const int T = (G - wave + NW - 1) / NW;
   const int64_t xrow = ok ? row : M - 1;
   XRaw8<XF32> ring[DEPTH];
   DownRaw<RB, PRE> dring[DEPTH];
   SmoothRaw8 sring[DEPTH];
   auto fetch = [&](int tt, int sl_) __attribute__((always_inline)) {
     const int tc = tt < T ? tt : T - 1;
-    const int gg = tc >= 0 ? wave + WAVES * tc : 0;
+    const int gg = tc >= 0 ? wave + NW * tc : 0;
     load_raw8<XF32>(X, xrow * K + gg * 64 + 8 * c, ring[sl_]);
     load_smooth8(smooth, gg * 64 + 8 * c, sring[sl_]);
     load_down<RB, PRE>(down, K, lane, gg * 64, dring[sl_]);
@@ -706,7 +708,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
   for (int sl = 0; sl < DEPTH; ++sl) {
     const int t = t0 + sl;
     const bool live = t < T;
-    const int g = wave + WAVES * (live ? t : T - 1);
+    const int g = wave + NW * (live ? t : T - 1);
     float x[8];
     uint32_t b[4];
     unpack_raw8<XF32>(ring[sl], ok && live, x, b);
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows8_kernel(
       const int rr = idx / R, cc = idx % R;
       float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < 2 * WAVES; ++w) sum += red[(w * 8 + rr) * R + cc];
+      for (int w = 0; w < 2 * NW; ++w) sum += red[(w * 8 + rr) * R + cc];
       if (row0 + rr < M) LR[(row0 + rr) * R + cc] = f32_to_bf16(sum);
     }
   }
@@ -871,12 +873,41 @@ constexpr size_t lds_bytes(int RB, bool pre) {
                 : 0;
 }
 
+// the 8-row kernel's LR partials and lora_down tiles (NW waves)
+constexpr size_t lds_bytes8(int RB, int NW) {
+  return RB > 0 ? size_t(NW) * 16 * RB * 16 * sizeof(float) + size_t(NW) * RB * 16 * DOWN_ROW
+                : 0;
+}
+
+// 8-row workgroups of 4 waves where there are at least two per CU and a
+// low-rank branch: two or three of them share a CU, and the extra
+// workgroups in flight hide more of the lora_down streaming.  With fewer
+// rows, or without the branch, 8 waves per workgroup keep more X loads in
+// flight.
+bool use_waves4(int M, int RB) {
+  return RB > 0 && (int64_t(M) + ROWS8 - 1) / ROWS8 >= 2 * int64_t(cu_count());
+}
+
 // dynamic LDS beyond the default 64 KB needs the kernel's opt-in
 svdq_status lds_opt_in(const void* fn, size_t shm, const char* what) {
   if (shm > 65536 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
     return svdq::fail(SVDQ_ERR_HIP, std::string(what) + ": shared memory size");
   return SVDQ_OK;
+}
+
+template <int RB, int XIN, bool FP4, int NW>
+svdq_status launch_rows8(const void* X, int M, int K, const float* smooth, const uint16_t* down,
+                         const float* ts_x, uint8_t* codes, void* scales, uint16_t* LR,
+                         hipStream_t s) {
+  const char* what = FP4 ? "act_quant_nvfp4" : "act_quant_int4";
+  const auto fn = act_quant_rows8_kernel<RB, XIN, FP4, NW>;
+  const size_t shm = lds_bytes8(RB, NW);
+  const svdq_status st = lds_opt_in(reinterpret_cast<const void*>(fn), shm, what);
+  if (st != SVDQ_OK) return st;
+  hipLaunchKernelGGL(fn, dim3((M + ROWS8 - 1) / ROWS8), dim3(64 * NW), shm, s, X, M, K, smooth,
+                     down, ts_x, codes, scales, LR);
+  return svdq::check_launch(what);
 }
 
 template <int RB, int XIN>
@@ -886,13 +917,12 @@ struct Int4Launch {
                         hipStream_t s) {
     if constexpr (RB <= RB_PREFETCH8) {
       if (use_rows8(M, RB)) {
-        const auto fn = act_quant_rows8_kernel<RB, XIN, false>;
-        const size_t shm = lds_bytes(RB, true);
-        const svdq_status st = lds_opt_in(reinterpret_cast<const void*>(fn), shm, "act_quant_int4");
-        if (st != SVDQ_OK) return st;
-        hipLaunchKernelGGL(fn, dim3((M + ROWS8 - 1) / ROWS8), dim3(64 * WAVES), shm, s, X, M, K,
-                           smooth, down, nullptr, codes, static_cast<void*>(scales), LR);
-        return svdq::check_launch("act_quant_int4");
+        if constexpr (RB > 0 && XIN != 1)   // fp32 X: the 4-wave kernel spills
+          if (use_waves4(M, RB))
+            return launch_rows8<RB, XIN, false, 4>(X, M, K, smooth, down, nullptr, codes, scales,
+                                                   LR, s);
+        return launch_rows8<RB, XIN, false, WAVES>(X, M, K, smooth, down, nullptr, codes, scales,
+                                                   LR, s);
       }
     }
     const auto fn = act_quant_int4_kernel<RB, XIN>;
@@ -912,13 +942,12 @@ struct Fp4Launch {
                         uint8_t* scales, uint16_t* LR, hipStream_t s) {
     if constexpr (RB <= RB_PREFETCH8) {
       if (use_rows8(M, RB)) {
-        const auto fn = act_quant_rows8_kernel<RB, XIN, true>;
-        const size_t shm = lds_bytes(RB, true);
-        const svdq_status st = lds_opt_in(reinterpret_cast<const void*>(fn), shm, "act_quant_nvfp4");
-        if (st != SVDQ_OK) return st;
-        hipLaunchKernelGGL(fn, dim3((M + ROWS8 - 1) / ROWS8), dim3(64 * WAVES), shm, s, X, M, K,
-                           smooth, down, ts_x, codes, static_cast<void*>(scales), LR);
-        return svdq::check_launch("act_quant_nvfp4");
+        if constexpr (RB > 0 && XIN != 1)   // fp32 X: the 4-wave kernel spills
+          if (use_waves4(M, RB))
+            return launch_rows8<RB, XIN, true, 4>(X, M, K, smooth, down, ts_x, codes, scales, LR,
+                                                  s);
+        return launch_rows8<RB, XIN, true, WAVES>(X, M, K, smooth, down, ts_x, codes, scales, LR,
+                                                  s);
       }
     }
     const auto fn = act_quant_nvfp4_kernel<RB, XIN>;
