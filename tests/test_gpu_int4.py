@@ -51,6 +51,15 @@ def test_act_quant_bf16_ragged_rows(m):
     _check_act(s["x"], lay, 32, bf16=True)
 
 
+@pytest.mark.parametrize("rank", [0, 32, 48])
+def test_act_quant_large_m(rank):
+    """M 4104 (a ragged tail past 16 x 256 rows): 8-row workgroups, of 4 waves
+    with the low-rank branch, lora_down prefetched at ranks 32 and 48."""
+    s = synth.layer(4104, 3072, 64, rank, seed=8, workload="attn")
+    lay = _oracle_layer(s["w"], s["x"], rank)
+    _check_act(s["x"], lay, rank, bf16=True)
+
+
 def test_act_quant_half_integer_ties():
     """Group amax 14 (scale 2, exact reciprocal) and 21 (scale 3, inexact
     reciprocal): every quotient that is a half-integer 0.5 ... 6.5, the values

@@ -75,6 +75,13 @@ def test_nvfp4_act_quant_bf16_ragged_rows(m):
     _check_act(s["x"], _oracle_layer(s["w"], s["x"], 32), 32, bf16=True)
 
 
+@pytest.mark.parametrize("rank", [32, 48])
+def test_nvfp4_act_quant_large_m(rank):
+    """M 4104: 8-row 4-wave workgroups with prefetched lora_down."""
+    s = synth.layer(4104, 3072, 64, rank, seed=12, workload="mlp_fp4")
+    _check_act(s["x"], _oracle_layer(s["w"], s["x"], rank), rank, bf16=True)
+
+
 def test_nvfp4_act_quant_grid_midpoints():
     """Block amax 12 with tensor scale 1 gives the block scale 2.0, so the
     quotients z / 2 are exact: every E2M1 midpoint (0.25 ... 5), one ulp on
