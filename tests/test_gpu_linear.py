@@ -101,15 +101,16 @@ def _mlp(seed):
     return m.cuda()
 
 
-def test_patched_block_follows_float_and_reloads(tmp_path):
-    print("patched MLP 2x96x256 (up / GELU-fused down / AWQ gate)", flush=True)
+@pytest.mark.parametrize("prec", ["int4", "nvfp4"])
+def test_patched_block_follows_float_and_reloads(tmp_path, prec):
+    print(f"patched MLP 2x96x256 (up / GELU-fused down / AWQ gate), {prec}", flush=True)
     model = _mlp(4)
     x = _x(192, 256, 5).reshape(2, 96, 256)
     with torch.no_grad():
         y_float = model(x.float())
     amax = L.calibrate(model, lambda: model(x.float()))
     assert set(amax) == {"up", "down", "gate"}
-    done = L.quantize_linears(model, amax, rank=32, awq={"gate"}, gelu_input={"down"})
+    done = L.quantize_linears(model, amax, rank=32, prec=prec, awq={"gate"}, gelu_input={"down"})
     assert done == {"up": "svdq", "down": "svdq", "gate": "awq"}
     model.act = nn.Identity()                       # the GELU now runs inside `down`
     with torch.no_grad():
