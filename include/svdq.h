@@ -214,8 +214,8 @@ svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, 
 
 /* LoRA folded into the 16-bit low-rank branch (offline, once per adapter).
  * A LoRA adapter adds scale * B (A x) to the layer's output; LoRA loading
- * keeps working on the quantized models ("Hugging Face Integrates Nunchaku
- * Lite for Native 4-bit Diffusion Inference", Broader Ecosystem Impact).
+ * keeps working on the quantized models (aiphreaks.com page, "Bringing
+ * Nunchaku 4-bit Diffusion Inference to Diffusers", Broader Ecosystem Impact).
  * The branch already reads raw X in 16 bits, so the adapter is a longer
  * rank:
  *   lora_down_out [r_new, K] = rows of lora_down, then rows of A, then zeros

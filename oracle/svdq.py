@@ -298,8 +298,9 @@ def gelu_input(x):
 def fold_lora(lora_down, lora_up, a, b, scale=1.0):
     """A LoRA adapter scale * B A (A [r_lora, K], B [N, r_lora], bf16 values)
     folded into the 16-bit low-rank branch by rank concatenation (LoRA loading
-    keeps working on the quantized models: "Hugging Face Integrates Nunchaku
-    Lite for Native 4-bit Diffusion Inference", Broader Ecosystem Impact).
+    keeps working on the quantized models: aiphreaks.com page, "Bringing
+    Nunchaku 4-bit Diffusion Inference to Diffusers", Broader Ecosystem
+    Impact).
     The branch reads raw X, as the adapter does, so
 
       lora_down' = [lora_down ; A ; 0],  lora_up' = [lora_up | bf16(fl32(scale B)) | 0]

@@ -5,10 +5,10 @@
 // (X lora_down^T) lora_up^T that reads the raw activations, so the adapter
 // becomes more rows of lora_down and more columns of lora_up: the branch
 // computes sum_i LR[m,i] lora_up[n,i] over the longer rank, and nothing in
-// the kernels changes but r.  ("Hugging Face Integrates Nunchaku Lite for
-// Native 4-bit Diffusion Inference", Broader Ecosystem Impact: LoRA loading
-// keeps working on the quantized models; "Bringing Nunchaku 4-bit Diffusion
-// Inference to Diffusers": the low-rank branch stays in 16 bits.)
+// the kernels changes but r.  (aiphreaks.com page, "Bringing Nunchaku 4-bit
+// Diffusion Inference to Diffusers": Broader Ecosystem Impact, LoRA loading
+// keeps working on the quantized models; Technical Breakdown and Performance
+// Metrics, the low-rank branch stays in 16 bits.)
 //
 // One launch writes both outputs element by element; the rank is padded to
 // the kernels' granularity of 16 with zero rows and columns, which add

@@ -4,8 +4,8 @@ quantized-layer file format.
 The lite integration does not ship model-specific fused kernels: it swaps
 the nn.Linear modules of an ordinary model for runtime SVDQ (W4A4) or AWQ
 (W4A16) layers (chaosnode.de page, "Nunchaku Lite vs. Original";
-"Hugging Face Integrates Nunchaku Lite for Native 4-bit Diffusion
-Inference", Technical Breakdown and Performance Metrics).  Here:
+aiphreaks.com page, "Bringing Nunchaku 4-bit Diffusion Inference to
+Diffusers", Technical Breakdown and Performance Metrics).  Here:
 
   SVDQLinear      one quantized layer held as device tensors; forward runs
                   svdq_linear_w4a4 (or its GELU-input form) on the current
