@@ -83,11 +83,13 @@ def test_act_quantize_gelu_int4():
     _int4_check(s["x"], lay, 32)
 
 
-def test_act_quantize_gelu_int4_rows8_and_ragged():
-    """M 4100: the 8-row workgroups, a ragged last block; rank 16."""
+@pytest.mark.parametrize("rank", [16, 48])
+def test_act_quantize_gelu_int4_rows8_and_ragged(rank):
+    """M 4100: 8-row workgroups of 4 waves, a ragged last block; rank 16,
+    and rank 48 with lora_down prefetched (a LoRA-folded layer's rank)."""
     s = synth.layer(4100, 640, 16, 0, seed=6, workload="mlp")
-    lay = random_int4_layer(64, 640, 16, seed=6, workload="mlp")
-    _int4_check(s["x"], lay, 16)
+    lay = random_int4_layer(64, 640, rank, seed=6, workload="mlp")
+    _int4_check(s["x"], lay, rank)
 
 
 def test_act_quantize_gelu_nvfp4():
