@@ -257,7 +257,8 @@ def other_paths(steps):
         "linear_us": round(t_lin_l * 1e6, 2),
         "linear_without_lora_us": round(t_lin_p * 1e6, 2),
         "fold_us": round(t_fold * 1e6, 2),
-        "fold_GB/s": round(fold_bytes / t_fold / 1e9, 1),
+        "fold_timing": "per Python call, including its two output allocations (host-bound)",
+        "fold_bytes": fold_bytes,
     }
     del x, lay, y, ws, codes, scales, lr, lay_l, ws_l, at, bt
     torch.cuda.empty_cache()
