@@ -155,7 +155,7 @@ def other_paths(steps):
     that the 256 MB last-level cache cannot hold them."""
     import numpy as np
     import torch
-    from w4a4_quantized_diffusion_amd import svdq, synth
+    from w4a4_quantized_diffusion_amd import svdq, synth, layout
     dev = torch.device("cuda:0")
     res = {}
 
@@ -209,8 +209,7 @@ def other_paths(steps):
     lay = dict(rank=R, prec=svdq.INT4, N=N, K=K, smooth=torch.from_numpy(r["smooth"]).to(dev),
                lora_down=torch.from_numpy(r["lora_down_bits"].view("int16")).to(dev),
                lora_up=torch.from_numpy(r["lora_up_bits"].view("int16")).to(dev),
-               wcodes=torch.from_numpy(np.ascontiguousarray(
-                   r["wcodes"].reshape(N, K // 64, 32).transpose(1, 0, 2))).to(dev),
+               wcodes=torch.from_numpy(layout.int4_to_device(r["wcodes"])).to(dev),
                wscales=torch.from_numpy(np.ascontiguousarray(r["sW"].T)).to(dev),
                w_tensor_scale=torch.ones(1, device=dev), x_tensor_scale=torch.ones(1, device=dev))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)

@@ -42,11 +42,19 @@
  * Formats
  * -------
  *  bf16 values are passed as uint16_t bit patterns.
- *  INT4 codes: sign-magnitude nibbles (bit 3 = sign, bits 0..2 = |q|, zero is
- *  0x0), values -7..7, two per byte, even k in the low nibble.  Group-major
- *  layout [K/64][rows][32 bytes]: the 64 codes of (group g, row r) are the 32
- *  bytes at offset (g * rows + r) * 32, so a GEMM tile's loads of one group
- *  are contiguous.
+ *  INT4 codes, values -7..7, four bits each, group-major layout
+ *  [K/64][rows][32 bytes]: the 64 codes of (group g, row r) are the 32 bytes
+ *  at offset (g * rows + r) * 32, so a GEMM tile's loads of one group are
+ *  contiguous.  Within them, the "fold" format: four 8-byte chunks; chunk c
+ *  holds the codes k = 64g + 8c + j as fields j and k = 64g + 32 + 8c + j as
+ *  fields 8 + j (j = 0..7).  Field f is the 6-bit pattern |q| | (q < 0) << 5
+ *  (q as an FP6-E2M3 subnormal q/8; a zero is 0, never a negative zero) at
+ *  bits 6f .. 6f+5 of a 96-bit string with 32-bit words o0, o1, o2.  The chunk
+ *  holds two little-endian words, X = o0 | (o1 & 0x18618618) then
+ *  Y = o2 | (o1 & 0x61861861): the masks are the exponent bits of o0's and
+ *  o2's fields, which are zero, and together exactly o1's payload bits, so
+ *  o0 = X & ~0x18618618, o2 = Y & ~0x61861861, o1 = (X & 0x18618618) |
+ *  (Y & 0x61861861) restore the GEMM's FP6 operand.
  *  INT4 group scales: float32, group-major [K/64][rows], scale =
  *  fl32(absmax / 7).
  *  NVFP4 codes: E2M1 nibbles (bit 3 = sign), same packing and the same
@@ -126,7 +134,8 @@ svdq_status svdq_act_absmax(const void* X, svdq_dtype x_dtype, int64_t M, int64_
  * rank: 0 <= rank <= min(N, K).  K % 64 == 0.
  * Outputs (DEVICE): smooth f32 [K]; lora_down bf16 [rank, K]; lora_up bf16
  * [N, rank] (inputs instead when flags has SVDQ_LOWRANK_GIVEN); wcodes u8
- * N*K/2 bytes, chunk-major [K/64][N][32]; wscales (INT4: f32 [K/64][N];
+ * N*K/2 bytes, group-major [K/64][N][32] (INT4: fold format; NVFP4: E2M1
+ * nibbles); wscales (INT4: f32 [K/64][N];
  * NVFP4: E4M3 u8 [K/64][N][4]); w_tensor_scale, x_tensor_scale f32 [1]
  * (NVFP4 only; may be NULL for INT4); residual f32 [N, K] or NULL.
  * Temporary device memory is allocated and freed inside the call. */
@@ -176,17 +185,18 @@ svdq_status svdq_gemm_w4a4(const uint8_t* codes, const void* scales, const uint1
                            hipStream_t stream);
 
 /* The whole layer: svdq_act_quantize into the workspace, then
- * svdq_gemm_w4a4, on one stream.  bias has x_dtype.  workspace: DEVICE, at
- * least svdq_workspace_bytes(M, K, rank, prec) bytes, 256-byte aligned, not
- * overlapping X or Y. */
+ * svdq_gemm_w4a4, on one stream.  bias: DEVICE [N] of bias_dtype (f32 or
+ * bf16, added in fp32 before the output conversion) or NULL (bias_dtype is
+ * then ignored).  workspace: DEVICE, at least svdq_workspace_bytes(M, K,
+ * rank, prec) bytes, 256-byte aligned, not overlapping X or Y. */
 svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
                              int64_t N, int32_t rank, svdq_precision prec,
                              const float* smooth, const uint16_t* lora_down,
                              const uint16_t* lora_up, const uint8_t* wcodes,
                              const void* wscales, const float* w_tensor_scale,
                              const float* x_tensor_scale, const void* bias,
-                             void* Y, svdq_dtype y_dtype, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream);
+                             svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The MLP down-projection's input form: the same calls with X replaced by
  * GELU(X), fused into the activation pass (the original engine's fused
@@ -209,8 +219,9 @@ svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, 
                                   const uint16_t* lora_up, const uint8_t* wcodes,
                                   const void* wscales, const float* w_tensor_scale,
                                   const float* x_tensor_scale, const void* bias,
-                                  void* Y, svdq_dtype y_dtype, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream);
+                                  svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /* LoRA folded into the 16-bit low-rank branch (offline, once per adapter).
  * A LoRA adapter adds scale * B (A x) to the layer's output; LoRA loading

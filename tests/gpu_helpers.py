@@ -52,6 +52,66 @@ def rm_codes(gm):
     return np.ascontiguousarray(gm.transpose(1, 0, 2).reshape(rows, g * 32))
 
 
+# INT4 device codes ("fold" format, from its definition in include/svdq.h):
+# chunk c of a row's 32 bytes per group holds k = 8c + j as field j and
+# k = 32 + 8c + j as field 8 + j; field f (|q| in bits 0..2, sign in bit 5)
+# sits at bits 6f.. of a 96-bit string o0 | o1 << 32 | o2 << 64, stored as
+# X = o0 | (o1 & GX), Y = o2 | (o1 & GY).  Written here with explicit bit
+# arrays, independently of the package's converter.
+_GX, _GY = 0x18618618, 0x61861861
+_W32 = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+
+
+def _chunk_codes(q):
+    """q [rows, K] -> [K/64, rows, 4 chunks, 16 fields] codes."""
+    rows, k = q.shape
+    g = k // 64
+    out = np.empty((g, rows, 4, 16), dtype=np.int64)
+    for c in range(4):
+        for j in range(8):
+            out[:, :, c, j] = q[:, 8 * c + j::64].T
+            out[:, :, c, 8 + j] = q[:, 32 + 8 * c + j::64].T
+    return out
+
+
+def gm_int4(packed):
+    """Oracle INT4 codes (textbook sign-magnitude nibbles [rows, K/2]) ->
+    device fold format [K/64, rows, 32] bytes."""
+    q = O.unpack_int4(np.asarray(packed, dtype=np.uint8)).astype(np.int64)
+    cq = _chunk_codes(q)
+    pat = np.abs(cq) | ((cq < 0).astype(np.int64) << 5)         # 6-bit fields
+    bits = ((pat[..., None] >> np.arange(6)) & 1).reshape(cq.shape[:-1] + (96,))
+    words = (bits.reshape(bits.shape[:-1] + (3, 32)).astype(np.uint64) * _W32).sum(-1)
+    o0, o1, o2 = words[..., 0], words[..., 1], words[..., 2]
+    x = o0 | (o1 & np.uint64(_GX))
+    y = o2 | (o1 & np.uint64(_GY))
+    xy = np.stack([x, y], axis=-1).astype("<u4")                # [g, rows, 4, 2]
+    return np.ascontiguousarray(xy.view(np.uint8).reshape(q.shape[1] // 64, q.shape[0], 32))
+
+
+def rm_int4(dev):
+    """Device fold-format codes [K/64, rows, 32] -> textbook nibbles
+    [rows, K/2], keeping the sign bit of a zero magnitude (so a negative zero
+    shows as 0x8 and fails a comparison with the oracle's codes)."""
+    dev = np.ascontiguousarray(np.asarray(dev, dtype=np.uint8))
+    g, rows, _ = dev.shape
+    w = dev.view("<u4").reshape(g, rows, 4, 2).astype(np.uint64)
+    x, y = w[..., 0], w[..., 1]
+    o0 = x & np.uint64(~_GX & 0xFFFFFFFF)
+    o1 = (x & np.uint64(_GX)) | (y & np.uint64(_GY))
+    o2 = y & np.uint64(~_GY & 0xFFFFFFFF)
+    words = np.stack([o0, o1, o2], axis=-1)                     # [g, rows, 4, 3]
+    bits = ((words[..., None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)).astype(np.int64)
+    fb = bits.reshape(g, rows, 4, 16, 6)
+    nib = fb[..., 0] | (fb[..., 1] << 1) | (fb[..., 2] << 2) | (fb[..., 5] << 3)
+    out = np.empty((rows, g * 64), dtype=np.uint8)
+    for c in range(4):
+        for j in range(8):
+            out[:, 8 * c + j::64] = nib[:, :, c, j].T
+            out[:, 32 + 8 * c + j::64] = nib[:, :, c, 8 + j].T
+    return (out[:, 0::2] | (out[:, 1::2] << 4)).astype(np.uint8)
+
+
 def gm_scales(s):
     return np.ascontiguousarray(np.asarray(s).T)
 
@@ -62,7 +122,7 @@ def layer_to_device(lay, rank, n, k, prec=0):
     d["smooth"] = t_f32(lay["smooth"])
     d["lora_down"] = t_bf16_bits(lay["lora_down"]) if rank else torch.zeros(1, dtype=torch.int16, device=dev())
     d["lora_up"] = t_bf16_bits(lay["lora_up"]) if rank else torch.zeros(1, dtype=torch.int16, device=dev())
-    d["wcodes"] = t_u8(gm_codes(lay["wcodes"]))
+    d["wcodes"] = t_u8(gm_int4(lay["wcodes"]))
     d["wscales"] = t_f32(gm_scales(lay["sW"]))
     d["w_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev())
     d["x_tensor_scale"] = torch.ones(1, dtype=torch.float32, device=dev())

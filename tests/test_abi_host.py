@@ -92,7 +92,7 @@ def test_gemm_rejects_bad_n(lib):
 def test_linear_rejects_small_workspace(lib):
     p = ctypes.c_void_p
     st = lib.svdq_linear_w4a4(p(0x10000), 1, 64, 128, 64, 16, 0, p(0x20000), p(0x30000),
-                              p(0x40000), p(0x50000), p(0x60000), None, None, None,
+                              p(0x40000), p(0x50000), p(0x60000), None, None, None, 0,
                               p(0x70000), 0, p(0x100000), 100, None)
     assert st == INVALID and "workspace too small" in svdq.svdq_last_error()
 
@@ -101,7 +101,7 @@ def test_linear_rejects_overlap(lib):
     p = ctypes.c_void_p
     need = svdq.svdq_workspace_bytes(64, 128, 16, "int4")
     st = lib.svdq_linear_w4a4(p(0x100000), 1, 64, 128, 64, 16, 0, p(0x20000), p(0x30000),
-                              p(0x40000), p(0x50000), p(0x60000), None, None, None,
+                              p(0x40000), p(0x50000), p(0x60000), None, None, None, 0,
                               p(0x900000), 0, p(0x100000), need, None)
     assert st == INVALID and "overlap" in svdq.svdq_last_error()
 
@@ -148,7 +148,7 @@ def test_gelu_forms_take_bf16_only(lib):
                                     None)
     assert st == UNSUPPORTED and "bf16" in svdq.svdq_last_error()
     st = lib.svdq_linear_w4a4_gelu(None, 0, 64, 128, 64, 16, 0, None, None, None, None, None,
-                                   None, None, None, None, 1, None, 0, None)
+                                   None, None, None, 0, None, 1, None, 0, None)
     assert st == UNSUPPORTED and "bf16" in svdq.svdq_last_error()
     # bf16 with bad shapes / NULL pointers: the usual validation
     st = lib.svdq_act_quantize_gelu(None, 1, 64, 100, 16, 0, None, None, None, None, None, None,

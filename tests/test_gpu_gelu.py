@@ -18,7 +18,7 @@ from oracle import nvfp4 as O4
 from oracle import formats as F
 from w4a4_quantized_diffusion_amd import svdq, synth
 from tests.gpu_helpers import (t_f32, t_x, t_u8, t_bf16_bits, layer_to_device, random_int4_layer,
-                               assert_y_close, rm_codes, gm_codes, bf16_bits_np)
+                               assert_y_close, rm_int4, rm_codes, bf16_bits_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def _int4_check(x, lay, rank):
     gm = group_mask(amb, 64)
     assert gm.mean() < 0.15, f"{gm.mean():.3%} of the groups are ambiguous"
     qx, sa = O.quantize_activations(xg, lay["smooth"])
-    got_c = rm_codes(codes.cpu().numpy()).reshape(m, k // 64, 32)
+    got_c = rm_int4(codes.cpu().numpy()).reshape(m, k // 64, 32)
     ref_c = O.pack_int4(qx).reshape(m, k // 64, 32)
     keep = ~gm
     assert np.array_equal(got_c[keep], ref_c[keep]), "codes differ outside ambiguous groups"
@@ -114,7 +114,7 @@ def test_act_quantize_gelu_nvfp4():
     gm = group_mask(amb, 16)
     assert gm.mean() < 0.05
     e, sb = O4.quantize_activations(xg, lay["smooth"], ts_x)
-    got_c = rm_codes(codes.cpu().numpy())                       # [m, k/2] bytes
+    got_c = rm_codes(codes.cpu().numpy())                      # [m, k/2] bytes
     ref_c = O.pack_nibbles(e)
     keep_bytes = np.repeat(~gm, 8, axis=1)                      # 8 bytes per block of 16
     assert np.array_equal(got_c[keep_bytes], ref_c[keep_bytes]), "E2M1 codes differ"

@@ -13,7 +13,7 @@ from oracle import svdq as O
 from oracle import formats as F
 from w4a4_quantized_diffusion_amd import linear as L
 from w4a4_quantized_diffusion_amd import svdq, synth
-from tests.gpu_helpers import rm_codes, bf16_bits_np, assert_y_close
+from tests.gpu_helpers import rm_int4, bf16_bits_np, assert_y_close
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def _x(m, k, seed):
 def _oracle_layer(mod):
     """The device layer of an INT4 SVDQLinear in the oracle's dict form."""
     d = dict(smooth=mod.smooth.cpu().numpy(),
-             q=O.unpack_int4(rm_codes(mod.wcodes.cpu().numpy())),
+             q=O.unpack_int4(rm_int4(mod.wcodes.cpu().numpy())),
              sW=np.ascontiguousarray(mod.wscales.cpu().numpy().T))
     if mod.rank:
         d["lora_down"] = F.bf16_to_f32(bf16_bits_np(mod.lora_down)).astype(np.float64)
@@ -55,11 +55,12 @@ def test_svdq_linear_matches_abi_and_oracle():
     y = mod(x)
     assert y.shape == (2, 150, 272) and y.dtype == torch.bfloat16
     ws = torch.empty(svdq.svdq_workspace_bytes(300, 512, 32), dtype=torch.uint8, device="cuda")
-    y_abi = svdq.svdq_linear_w4a4(x.reshape(300, 512), mod.layer(), lin.bias.detach().to(torch.bfloat16),
+    # the module adds its fp32 bias through the C entry point's bias_dtype
+    y_abi = svdq.svdq_linear_w4a4(x.reshape(300, 512), mod.layer(), lin.bias.detach().float(),
                                   y_dtype=torch.bfloat16, workspace=ws)
     assert torch.equal(y.reshape(300, 272), y_abi)
     xb = x.reshape(300, 512).float().cpu().numpy()
-    bias = synth.round_bf16(lin.bias.detach().cpu().numpy())
+    bias = lin.bias.detach().cpu().numpy().astype(np.float64)
     y_ref, _ = O.linear_w4a4(xb, _oracle_layer(mod), bias)
     assert_y_close(y.reshape(300, 272), y_ref, True, "SVDQLinear")
     # fp32 input, fp32 output, same layer
@@ -118,9 +119,9 @@ def test_patched_block_follows_float_and_reloads(tmp_path, prec):
     err = ((y.float() - y_float).norm() / y_float.norm()).item()
     assert err < 0.08, err
     # the same result from the modules' C entry points one by one
-    h = svdq.svdq_linear_w4a4(x.reshape(192, 256), model.up.layer(), model.up.bias.to(torch.bfloat16),
+    h = svdq.svdq_linear_w4a4(x.reshape(192, 256), model.up.layer(), model.up.bias,
                               y_dtype=torch.bfloat16)
-    d = svdq.svdq_linear_w4a4_gelu(h, model.down.layer(), model.down.bias.to(torch.bfloat16),
+    d = svdq.svdq_linear_w4a4_gelu(h, model.down.layer(), model.down.bias,
                                    y_dtype=torch.bfloat16)
     g = svdq.awq_linear_w4a16(x.reshape(192, 256), dict(q=model.gate.q, scales=model.gate.scales,
                                                         zeros=model.gate.zeros, N=256, K=256,

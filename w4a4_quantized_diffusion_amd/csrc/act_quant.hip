@@ -9,8 +9,10 @@
 //   per block: E4M3 block scale, E2M1 codes      (NVFP4, blocks of 16)
 //   LR = bf16(X) . lora_down^T                   (low-rank down-projection)
 //
-// Output layout: chunk-major along K, codes[K/64][M][32 bytes]; scales
-// [K/64][M] (INT4, f32) or [K/64][M][4] (NVFP4, E4M3 bytes).
+// Output layout: group-major along K, codes[K/64][M][32 bytes] (INT4 in the
+// fold format of the GEMM's FP6 operand: chunk c, 8 bytes, holds the codes
+// 8c + j and 32 + 8c + j, j = 0..7; NVFP4 as E2M1 nibbles); scales [K/64][M]
+// (INT4, f32) or [K/64][M][4] (NVFP4, E4M3 bytes).
 //
 // Work split: a workgroup of 8 waves owns 16 rows; wave w takes the K-groups
 // w, w+8, ... so that at every step the 8 waves read adjacent 128-byte
@@ -203,25 +205,35 @@ __device__ __forceinline__ bool near_half_r(float t, float r) {
   return fabsf(r - fabsf(t)) >= 0.5f - 0x1p-19f;
 }
 
-// Sign-magnitude INT4 code of t (|t| < 7.5) as a float, given r = rne(|t|):
-// r + 8 when t < -1/2 (a negative value with a nonzero magnitude).  The
-// clamped fma is 2^24 (-t - 1/2) limited to [0, 1]: 1 for any t below -1/2
-// (the binary32 spacing there is at least 2^-24), 0 otherwise.
-__device__ __forceinline__ float int4_code(float t, float r) {
+// INT4 code of t (|t| < 7.5), given r = rne(|t|), as its 6-bit field of the
+// fold format: |q| in bits 0..2, the sign in bit 5 (set when t < -1/2, a
+// negative value with a nonzero magnitude).  The clamped fma is
+// 2^24 (-t - 1/2) limited to [0, 1]: 1 for any t below -1/2 (the binary32
+// spacing there is at least 2^-24), 0 otherwise.
+__device__ __forceinline__ uint32_t int4_field(float t, float r) {
   const float neg = __builtin_amdgcn_fmed3f(fmaf(t, -0x1p24f, -0x1p23f), 0.0f, 1.0f);
-  return fmaf(neg, 8.0f, r);
+  return uint32_t(fmaf(neg, 32.0f, r));
 }
 
-// eight codes (value j in nibble j: the even values in the low nibbles) into
-// one word; each code goes into a byte with v_cvt_pk_u8_f32
-__device__ __forceinline__ uint32_t int4_word(const float (&t)[8], const float (&r)[8]) {
-  uint32_t e = 0, o = 0;
+// Eight codes as fields 0..7 of a 96-bit field string, 6 bits apart: bits
+// 0..31 in lo, 32..47 in the low half of hi.
+__device__ __forceinline__ void int4_fields48(const float (&t)[8], const float (&r)[8],
+                                              uint32_t& lo, uint32_t& hi) {
+  uint32_t f[8];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    e = __builtin_amdgcn_cvt_pk_u8_f32(int4_code(t[2 * b], r[2 * b]), b, e);
-    o = __builtin_amdgcn_cvt_pk_u8_f32(int4_code(t[2 * b + 1], r[2 * b + 1]), b, o);
-  }
-  return e | (o << 4);
+  for (int j = 0; j < 8; ++j) f[j] = int4_field(t[j], r[j]);
+  lo = f[0] | (f[1] << 6) | (f[2] << 12) | (f[3] << 18) | (f[4] << 24) | (f[5] << 30);
+  hi = (f[5] >> 2) | (f[6] << 4) | (f[7] << 10);
+}
+
+// Fold format of one chunk of 16 codes (fields 0..7: lo0, hi0; fields 8..15:
+// lo1, hi1): the field string's words o0, o1, o2 stored as two words, the
+// middle word's payload bits in the zero exponent bits of the outer two.
+constexpr uint32_t FOLD_GX = 0x18618618u, FOLD_GY = 0x61861861u;
+__device__ __forceinline__ uint2 int4_fold(uint32_t lo0, uint32_t hi0, uint32_t lo1,
+                                           uint32_t hi1) {
+  const uint32_t o0 = lo0, o1 = hi0 | (lo1 << 16), o2 = (lo1 >> 16) | (hi1 << 16);
+  return make_uint2(o0 | (o1 & FOLD_GX), o2 | (o1 & FOLD_GY));
 }
 
 // NVFP4 by the hardware conversions (v_cvt_scalef32_pk_fp4_f32 rounds to the
@@ -403,7 +415,7 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     const float s = amax / 7.0f;
     const float inv = 1.0f / s;
     const bool fast = s >= 0x1p-126f;
-    uint32_t w0 = 0, w1 = 0;
+    uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
     if (s > 0.f) {
       // quotients through the reciprocal; only when some lane of the wave
       // has one within 2^-19 of a half-integer (or a tiny scale) does the
@@ -431,15 +443,15 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
           }
         }
       }
-      w0 = int4_word(t0, r0);
-      w1 = int4_word(t1, r1);
+      int4_fields48(t0, r0, lo0, hi0);
+      int4_fields48(t1, r1, lo1, hi1);
     }
     if (ok && live) {
       // group-major layout: the 32 bytes of (group g, row) follow those of
-      // (g, row - 1), so the GEMM's loads of a group are contiguous
-      uint32_t* cp = reinterpret_cast<uint32_t*>(codes + (int64_t(g) * M + row) * 32);
-      cp[q] = w0;
-      cp[4 + q] = w1;
+      // (g, row - 1), so the GEMM's loads of a group are contiguous; this
+      // lane's 16 codes are chunk q of the fold format
+      *reinterpret_cast<uint2*>(codes + (int64_t(g) * M + row) * 32 + 8 * q) =
+          int4_fold(lo0, hi0, lo1, hi1);
       if (q == 0) scales[int64_t(g) * M + row] = s;
     }
     if constexpr (PRE) {
@@ -729,7 +741,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 || RB > 2 ? 2 : 3) void act_quant_
       const float s = a / 7.0f;
       const float inv = 1.0f / s;
       const bool fast = s >= 0x1p-126f;
-      uint32_t w = 0;
+      uint32_t lo = 0, hi = 0;
       if (s > 0.f) {
         float tq[8], rq[8];
         bool need = !fast;
@@ -747,10 +759,15 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 || RB > 2 ? 2 : 3) void act_quant_
               rq[j] = rintf(fabsf(tq[j]));
             }
         }
-        w = int4_word(tq, rq);
+        int4_fields48(tq, rq, lo, hi);
       }
+      // chunk c of the fold format holds the 8-element chunks c and c + 4:
+      // this lane's fields and those of lane l + 32 (same row)
+      const uint32_t lo_up = __shfl_xor(lo, 32), hi_up = __shfl_xor(hi, 32);
       if (ok && live) {
-        cp[c] = w;
+        if (c < 4)
+          *reinterpret_cast<uint2*>(codes + (int64_t(g) * M + row) * 32 + 8 * c) =
+              int4_fold(lo, hi, lo_up, hi_up);
         if (c == 0) static_cast<float*>(scales)[int64_t(g) * M + row] = s;
       }
     } else {

@@ -10,26 +10,30 @@
 // of the aiphreaks.com page, "Technical Breakdown").
 //
 // Mapping to CDNA4:
-//  * A code q in -7..7 is exact in FP8-E4M3 as the subnormal q 2^-9 (the
-//    byte is the nibble's magnitude with the sign moved to bit 7, so the
-//    widening is three bit operations per four codes).  Every partial sum of
-//    a 64-long group of products is an integer multiple of 2^-18 below 2^-6,
-//    so one v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 = one group) with E8M0
-//    block scales of 2^9 on both operands returns I_g exactly, already as
-//    fp32.  The nibbles are widened while a tile is staged into LDS.
+//  * A code q in -7..7 is exact in FP6-E2M3 as the subnormal q 2^-3 (bits
+//    s 0 0 m m m: the exponent bits are zero).  Every partial sum of a
+//    64-long group of products is an integer multiple of 2^-6 below 2^6, so
+//    one v_mfma_scale_f32_32x32x64_f8f6f4 with FP6 operands (K = 64 = one
+//    group, at the FP4/FP6 rate, twice the FP8 one) and E8M0 block scales of
+//    2^3 on both operands returns I_g exactly, already as fp32.
+//  * Codes stay 4 bits in memory, in the fold format: the 96-bit string of
+//    sixteen 6-bit fields (three words o0, o1, o2) of a chunk of 16 codes is
+//    stored as two words X = o0 | (o1 & GX), Y = o2 | (o1 & GY).  GX and GY
+//    mark the exponent bits of o0 and o2, and together they are exactly the
+//    payload bits of o1, so four bit operations restore the MFMA operand.
 //  * The group scale is an outer product sA[:,g] sW[:,g]^T.  The kernel
 //    forms it on the matrix core too: the two-block 32x32x1 fp32 MFMA gives
 //    fl32(sA sW) for a row block and both column blocks of a wave at once, in
 //    the same register layout as I_g.  The vector ALU then does one FMA per
-//    element and group: acc += S (.) I.  (VALU fp32 issue is the other
-//    limited resource, so the scale product must not cost a second VALU op
-//    per element-group.)
+//    element and group: acc += S (.) I.  That FMA is the bound: at 16 fp32
+//    lanes per clock it takes as long per element-group as the INT8 / FP8
+//    MFMA peak, so every other vector operation is kept out of the loop.
 //  * The epilogue accumulates LR . lora_up^T into the same fp32 tile with
 //    32x32x16 bf16 MFMAs, adds the bias and converts.
 //
-// A and B operands of an MFMA use the same lane/byte -> k assignment, so any
-// permutation of k inside a group that is applied identically to both
-// operands leaves every product sum unchanged; the unpacker uses one.
+// A and B operands of an MFMA use the same lane/field -> k assignment, so
+// the order of k inside a group (the fold format's chunk layout) leaves
+// every product sum unchanged as long as both operands use it.
 
 #include "internal.h"
 
@@ -43,65 +47,52 @@ namespace {
 
 // ---------------------------------------------------------------- unpack
 
-// Eight sign-magnitude nibbles (one 32-bit word) -> eight E4M3 bytes that
-// hold the codes as subnormals: byte s000 0mmm is (-1)^s m 2^-9.  lo: bytes
-// of the even nibbles, hi: bytes of the odd nibbles.  The MFMA's E8M0 block
-// scales (2^9 on each operand) restore the integer products exactly.
-__device__ __forceinline__ void nib8_to_e4m3(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  lo = (w & 0x07070707u) | ((w << 4) & 0x80808080u);
-  hi = ((w >> 4) & 0x07070707u) | (w & 0x80808080u);
+// One chunk of 16 codes in the fold format (two words X, Y) -> the three
+// words of their FP6-E2M3 operand: field j (bits 6j .. 6j+5 of the 96-bit
+// string o0 | o1 << 32 | o2 << 64) holds code j as the subnormal
+// (-1)^s m 2^-3, bits s 0 0 m m m.  The two exponent bits of every field are
+// zero, and the fold format keeps the middle word's 21 payload bits in the
+// exponent slots of the outer two: GX marks the exponent bits of o0, GY those
+// of o2, and together they are exactly the payload bits of o1.
+constexpr uint32_t FOLD_GX = 0x18618618u, FOLD_GY = 0x61861861u;
+__device__ __forceinline__ void unfold16(uint32_t x, uint32_t y, uint32_t& o0, uint32_t& o1,
+                                         uint32_t& o2) {
+  o0 = x & ~FOLD_GX;
+  o2 = y & ~FOLD_GY;
+  o1 = (x & FOLD_GX) | (y & FOLD_GY);
 }
-constexpr int CODE_SCALE = 127 + 9;     // E8M0 2^9
+constexpr int CODE_SCALE = 127 + 3;     // E8M0 2^3 on each operand
+constexpr int FMT_FP6 = 2;              // f8f6f4 operand format: FP6 E2M3
 
 // --------------------------------------------------------------- tiling
 //
 // Workgroup tile 256 x 256, 8 waves (2 per SIMD) arranged 2 (M) x 4 (N), each
 // wave 128 x 64 = 4 x 2 blocks of 32 x 32 (128 fp32 accumulators per lane,
-// in VGPRs so the vector ALU can apply the group scales).  One K-group (64
-// codes) per pipeline step: while the waves run the MFMAs of group g out of
-// one LDS buffer, they widen the packed codes of group g+1 (DMA'd into LDS one
-// step earlier) into the other buffer and start the DMA of group g+2.  One
-// barrier per group.  LDS rows are padded to 80 bytes so that the 16
-// lanes of one ds_read_b128 phase (16 consecutive rows) hit distinct banks.
+// in VGPRs so the vector ALU can apply the group scales).  The packed codes
+// and scales of one K-group (64 codes) for the whole tile, 512 rows of 32
+// bytes, are DMA'd into one of NBUF LDS buffers, NBUF - 1 groups ahead of the
+// group the waves compute on; one barrier per group.  Each wave reads its
+// packed fragments (16 bytes per lane) straight from the buffer and decodes
+// them in registers (four bit operations per 16 codes), so codes are stored
+// once in LDS and never rewritten.
 
 constexpr int BM = 256, BN = 256;
 constexpr int NT = 512;
 constexpr int WM = 128, WN = 64;        // wave tile
 constexpr int RBL = WM / 32, CBL = WN / 32;
-constexpr int LDS_ROW = 80;             // 64 bytes of E4M3 codes + 16 pad
+constexpr int NBUF = 4;                 // LDS ring depth (groups)
 
-struct Stage {
-  uint8_t a[BM * LDS_ROW];
-  uint8_t b[BN * LDS_ROW];
-  float sa[BM];                         // group scales of the A rows
-  float sb[BN];                         // group scales of the B rows
-};
 
-// Packed codes and scales of one group, fetched global -> LDS by DMA.  Each
-// wave fetches the 64 rows it stages: 2 KB of codes in two contiguous 1 KB
-// transfers (lane L lands at base + 16 L), so row r of the wave sits at
-// code[wave][32 r], and the 64 scales in one transfer.
-struct Packed {
-  uint8_t code[NT / 64][64 * 32];
-  float scale[NT];
+// One group of the tile: rows 0..255 are the A rows, 256..511 the W rows.
+// Row r's two 16-byte halves h sit in 16-byte slots 2r + (h ^ s(r)), with
+// s(r) = bit 3 of r: the 16 lanes of one ds_read_b128 phase (rows r..r+15 of
+// one half) then hit 16 distinct bank groups.
+struct __attribute__((aligned(16))) Ring {
+  uint4 code[(BM + BN) * 2];
+  float scale[BM + BN];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// LDS stores at a compile-time byte offset from one address register (a
-// 16-byte store per pair of words: with 80-byte rows the 16 lanes of one
-// store phase hit distinct banks)
-template <int OFF>
-__device__ __forceinline__ void lds_store_b128(uint32_t addr, v4i d) {
-  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF));
-}
-// two packed words -> their 16 widened bytes
-__device__ __forceinline__ v4i widen16(uint32_t w0, uint32_t w1) {
-  uint32_t l0, h0, l1, h1;
-  nib8_to_e4m3(w0, l0, h0);
-  nib8_to_e4m3(w1, l1, h1);
-  return v4i{int(l0), int(h0), int(l1), int(h1)};
-}
 
 template <typename T>
 __device__ __forceinline__ float load_bias(const void* p, int64_t n);
@@ -114,12 +105,14 @@ __device__ __forceinline__ float load_bias<uint16_t>(const void* p, int64_t n) {
   return bf16_to_f32(static_cast<const uint16_t*>(p)[n]);
 }
 
-__device__ __forceinline__ v8i lds_frag(const uint8_t* base) {
-  const uint4 x = reinterpret_cast<const uint4*>(base)[0];
-  const uint4 y = reinterpret_cast<const uint4*>(base)[1];
-  return v8i{int(x.x), int(x.y), int(x.z), int(x.w), int(y.x), int(y.y), int(y.z), int(y.w)};
+// one lane's FP6 operand from its 16 packed bytes (two chunks of 16 codes):
+// six words (the MFMA reads the first six of eight)
+__device__ __forceinline__ v8i decode_frag(const uint4 w) {
+  uint32_t a0, a1, a2, b0, b1, b2;
+  unfold16(w.x, w.y, a0, a1, a2);
+  unfold16(w.z, w.w, b0, b1, b2);
+  return v8i{int(a0), int(a1), int(a2), int(b0), int(b1), int(b2), 0, 0};
 }
-
 
 template <int RK, bool YBF16, bool BBF16>
 __global__ __launch_bounds__(NT) void gemm_int4_kernel(
@@ -127,10 +120,9 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     const uint16_t* __restrict__ LR, int M, int K, int N,
     const uint8_t* __restrict__ W, const float* __restrict__ sW,
     const uint16_t* __restrict__ up, const void* __restrict__ bias, void* __restrict__ Y) {
-  // separate LDS objects, so that the compiler can tell the DMA targets apart
-  // from the buffers the MFMAs read (no waits on an in-flight DMA)
-  __shared__ Stage st0, st1;
-  __shared__ Packed pkb0, pkb1;
+  // separate LDS objects, so that the compiler can tell the buffer a DMA
+  // fills apart from the ones the waves read
+  __shared__ Ring rg0, rg1, rg2, rg3;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 2, wn = wave & 3;
@@ -145,93 +137,42 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
   const int G = K / 64;
 
-  // staging role: waves 0..3 stage the 256 A rows of the tile (64 each),
-  // waves 4..7 the 256 B rows; thread tid widens row tid % 256 of its side.
-  // Rows past the matrix edge fetch the last row instead: their products only
-  // reach accumulator rows / columns that are never stored, so the main loop
-  // needs neither branches nor masks.
+  // DMA role: wave w fills 16-byte slots 128 w .. 128 w + 127 (rows 64 w ..
+  // 64 w + 63: the A rows for w < 4, the W rows after) in two 1 KB transfers,
+  // and thread tid the scale of row tid.  Rows past the matrix edge fetch the
+  // last row instead: their products only reach accumulator rows / columns
+  // that are never stored, so the main loop needs neither branches nor masks.
   const bool is_a = wave < BM / 64;
-  const int srow = tid & (BM - 1);
   const int rows_total = is_a ? M : N;
-  const int64_t row0 = is_a ? m0 : n0;
-  const int soff = (is_a ? 0 : int(offsetof(Stage, b))) + srow * LDS_ROW;
-  const int sidx = (is_a ? int(offsetof(Stage, sa)) : int(offsetof(Stage, sb))) + srow * 4;
+  const int64_t row0 = is_a ? m0 : n0 - BM;
   const uint8_t* const gbase = is_a ? A : W;
   const float* const sbase = is_a ? sA : sW;
-  // per-lane byte offsets (within one group's slab) of the two code transfers
-  // and of the scale transfer
-  const int wrow = (wave & 3) * 64;
-  const int64_t rc0 = row0 + wrow + (lane >> 1), rs = row0 + wrow + lane;
-  const int last = rows_total - 1;
-  const uint32_t off0 = uint32_t(rc0 < rows_total ? rc0 : last) * 32u + (lane & 1) * 16u;
-  const uint32_t off1 = uint32_t(rc0 + 32 < rows_total ? rc0 + 32 : last) * 32u + (lane & 1) * 16u;
-  const uint32_t offs = uint32_t(rs < rows_total ? rs : last) * 4u;
+  const int64_t last = rows_total - 1;
+  int64_t coff[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int slot = 128 * wave + 64 * k + lane;
+    const int r = slot >> 1, half = (slot & 1) ^ ((r >> 3) & 1);
+    const int64_t gr = row0 + r;
+    coff[k] = (gr < rows_total ? gr : last) * 32 + 16 * half;
+  }
+  const int64_t srow = row0 + tid;
+  const int64_t soff = (srow < rows_total ? srow : last) * 4;
 
-  // DMA of one group's packed codes and scales into LDS; no registers are
-  // held while it is in flight
-  auto dma = [&](int g, Packed& pk) {
+  auto dma = [&](int g, Ring& rb) {
     const uint8_t* gg = gbase + int64_t(g) * rows_total * 32;
     const uint8_t* gs = reinterpret_cast<const uint8_t*>(sbase + int64_t(g) * rows_total);
-    __builtin_amdgcn_global_load_lds(gg + off0, (lds_ptr_t)&pk.code[wave][0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gg + off1, (lds_ptr_t)&pk.code[wave][1024], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gs + offs, (lds_ptr_t)&pk.scale[wave * 64], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gg + coff[0], (lds_ptr_t)&rb.code[128 * wave], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gg + coff[1], (lds_ptr_t)&rb.code[128 * wave + 64], 16, 0,
+                                     0);
+    __builtin_amdgcn_global_load_lds(gs + soff, (lds_ptr_t)&rb.scale[64 * wave], 4, 0, 0);
   };
-  // The staged row's 32 packed bytes.  Read in an asm block that waits for
-  // its own result: the compiler's wait-count tracking does not tell DMA
-  // targets apart and would otherwise wait for the DMA started this step.
-  auto fetch_words = [&](const Packed& pk, v4i& w0, v4i& w1) {
-    typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
-    const uint32_t addr = uint32_t(reinterpret_cast<uintptr_t>((lds_cptr)&pk.code[wave][lane * 32]));
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(w0), "=v"(w1) : "v"(addr));
-  };
-  auto fetch4 = [&](const Packed& pk, int half, v4i& w) {
-    typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
-    const uint32_t addr =
-        uint32_t(reinterpret_cast<uintptr_t>((lds_cptr)&pk.code[wave][lane * 32 + half * 16]));
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(w) : "v"(addr));
-  };
-  // widen packed words 2p, 2p+1 into 16 E4M3 bytes at LDS offset 16p
-  // LDS stores of the widened codes / scales go through asm as well:
-  // the compiler would wait for every DMA in flight before any LDS store.
-  typedef __attribute__((address_space(3))) uint8_t* lds_bptr;
-  auto lds_addr = [](void* p) { return uint32_t(reinterpret_cast<uintptr_t>((lds_bptr)p)); };
-  auto widen_all = [&](uint8_t* stage_base, const Packed& pk) {
-    v4i w0, w1;
-    fetch_words(pk, w0, w1);
-    const uint32_t a = lds_addr(stage_base + soff);
-    lds_store_b128<0>(a, widen16(uint32_t(w0[0]), uint32_t(w0[1])));
-    lds_store_b128<16>(a, widen16(uint32_t(w0[2]), uint32_t(w0[3])));
-    lds_store_b128<32>(a, widen16(uint32_t(w1[0]), uint32_t(w1[1])));
-    lds_store_b128<48>(a, widen16(uint32_t(w1[2]), uint32_t(w1[3])));
-  };
-  // the same, spread over the MFMA blocks: word pair p = 0..3
-  v4i pw;
-  auto widen_pair = [&](uint8_t* stage_base, int p) {
-    const uint32_t a = lds_addr(stage_base + soff);
-    switch (p) {
-      case 0:
-        lds_store_b128<0>(a, widen16(uint32_t(pw[0]), uint32_t(pw[1])));
-        break;
-      case 1:
-        lds_store_b128<16>(a, widen16(uint32_t(pw[2]), uint32_t(pw[3])));
-        break;
-      case 2:
-        lds_store_b128<32>(a, widen16(uint32_t(pw[0]), uint32_t(pw[1])));
-        break;
-      default:
-        lds_store_b128<48>(a, widen16(uint32_t(pw[2]), uint32_t(pw[3])));
-        break;
-    }
-  };
-  // the staged row's group scale, copied next to the widened codes (the
-  // packed buffer is refilled by DMA while the stage is in use)
-  auto stage_scale = [&](uint8_t* stage_base, const Packed& pk) {
-    float sv;
-    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(sv) : "v"(lds_addr((void*)&pk.scale[tid])));
-    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(stage_base + sidx)), "v"(sv));
-  };
+
+  // per-lane byte offsets of the fragment reads: row block base + the
+  // lane's (row, half) slot; the swizzle bit of row 32 b + r32 is bit 3 of r32
+  const int fslot = 2 * r32 + (h ^ ((r32 >> 3) & 1));
+  const int aoff = 2 * (wm * WM) + fslot;          // in 16-byte slots
+  const int boff = 2 * (BM + wn * WN) + fslot;
 
   v16f acc[RBL][CBL];
 #pragma unroll
@@ -247,119 +188,80 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
 #pragma unroll
   for (int e = 0; e < 32; ++e) zero32[e] = 0.f;
 
-  uint8_t* const stage0 = reinterpret_cast<uint8_t*>(&st0);
-  uint8_t* const stage1 = reinterpret_cast<uint8_t*>(&st1);
-
-  // the integer products of one block; the scale outer products of one row
-  // block (both column blocks) in S2
-  v16f P[1];
-  v32f S2;
-  v8i fb[CBL], fa;
-  float qa, qb;
-  auto load_b = [&](const Stage& cs) {
+  // One K-group out of buffer `cur`.  Per row block: the scale outer product
+  // fl32(sA sW) of its two column blocks (the two-block 32x32x1 fp32 MFMA
+  // takes rows from lanes 32 b + r and columns from lanes 32 b + c for block
+  // b: every lane passes its row's sA and the sW of column l of the wave
+  // tile), then per column block the exact integer products I_g and one FMA
+  // per element, acc += S (.) I.
+  auto compute = [&](const Ring& cur) {
+    v8i fb[CBL];
 #pragma unroll
-    for (int j = 0; j < CBL; ++j) {
-      const int rb = wn * WN + j * 32 + r32;
-      fb[j] = lds_frag(cs.b + rb * LDS_ROW + h * 32);
-    }
-    qb = cs.sb[wn * WN + lane];       // lane l: column l of the wave tile
-  };
-  auto load_fa = [&](const Stage& cs, int i) {
-    fa = lds_frag(cs.a + (wm * WM + i * 32 + r32) * LDS_ROW + h * 32);
-  };
-  auto load_qa = [&](const Stage& cs, int i) { qa = cs.sa[wm * WM + i * 32 + r32]; };
-  auto mfma_p = [&](int b) {          // block b = (i = b / 2, j = b % 2)
-    P[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[b & 1], zero, 0, 0, 0,
-                                                              CODE_SCALE, 0, CODE_SCALE);
-  };
-  // sA (x) sW for the current row block and both column blocks: the
-  // two-block 32x32x1 fp32 MFMA takes rows from lanes 32b + r and columns
-  // from lanes 32b + c for block b, so every lane passes its row's sA and
-  // sW of column l of the wave tile; block j lands in S2[16 j, 16 j + 16)
-  // in the usual 32x32 layout.  Each element is fl32(sA sW).
-  auto mfma_s2 = [&]() { S2 = __builtin_amdgcn_mfma_f32_32x32x1f32(qa, qb, zero32, 0, 0, 0); };
-  auto fma_block = [&](int b) {
-    const int i = b >> 1, j = b & 1;
+    for (int j = 0; j < CBL; ++j) fb[j] = decode_frag(cur.code[boff + 64 * j]);
+    const float qb = cur.scale[BM + wn * WN + lane];
+    v8i fa = decode_frag(cur.code[aoff]);
+    float qa = cur.scale[wm * WM + r32];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      acc[i][j][e] = fmaf(S2[16 * j + e], P[0][e], acc[i][j][e]);
-  };
-
-  // One K-group.  Per block b: the FMAs of block b (their scale products
-  // were formed one or two blocks earlier), the integer-product MFMA of block
-  // b+1, and at each new row block the two-block scale MFMA; the other wave
-  // on the SIMD keeps the matrix core busy while this one waits.  The FMAs of
-  // block 7 run after the barrier, while the next group's fragments load.
-  // The next group's codes are widened into `nxt` in between; on the last
-  // group this fills the idle buffer with data nobody reads, which keeps the
-  // loop body branch-free.
-  auto group_step = [&](const uint8_t* cur, uint8_t* nxt, const Packed& pk_next, Packed& pk_free,
-                        bool tail, int gdma) {
-    const Stage& cs = *reinterpret_cast<const Stage*>(cur);
-    dma(gdma, pk_free);                 // two groups ahead, into the buffer freed last step
-    load_b(cs);
-    load_fa(cs, 0);
-    load_qa(cs, 0);
-    if (tail) fma_block(7);             // previous group's last block
-    mfma_p(0);
-    mfma_s2();                          // row block 0
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < RBL; ++i) {
+      // the next row block's packed fragment and scale load while this one runs
+      uint4 fa_raw;
+      float qa_nxt;
+      if (i + 1 < RBL) {
+        fa_raw = cur.code[aoff + 64 * (i + 1)];
+        qa_nxt = cur.scale[wm * WM + (i + 1) * 32 + r32];
+      }
+      const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(qa, qb, zero32, 0, 0, 0);
+      v16f P[CBL];
 #pragma unroll
-    for (int b = 0; b < 7; ++b) {
-      const bool new_row = (b & 1) == 1;      // block b+1 starts row block (b+1)/2
-      // issue order is fixed with scheduling barriers.  One product buffer: the FMAs of block b read it before the MFMA of
-      // block b+1 overwrites it; the next row block's fragment and scale
-      // load only after that MFMA has taken the current ones
-      // the FMAs issue at raised wave priority, so that of the two waves on
-      // a SIMD the one with vector work ready goes first and the other's
-      // MFMA issue slips behind it: the pair drifts out of step
+      for (int j = 0; j < CBL; ++j)
+        P[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fa, fb[j], zero, FMT_FP6, FMT_FP6, 0, CODE_SCALE, 0, CODE_SCALE);
+      // the FMAs issue at raised wave priority: of the two waves on a SIMD,
+      // the one with vector work ready goes first and the other's MFMA issue
+      // slips behind it, so the pair drifts out of step
       __builtin_amdgcn_s_setprio(1);
-      fma_block(b);
+#pragma unroll
+      for (int j = 0; j < CBL; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(S[16 * j + e], P[j][e], acc[i][j][e]);
       __builtin_amdgcn_s_setprio(0);
-      mfma_p(b + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (!new_row && b + 2 < 8) {
-        load_fa(cs, (b + 2) >> 1);
-        load_qa(cs, (b + 2) >> 1);
+      if (i + 1 < RBL) {
+        fa = decode_frag(fa_raw);
+        qa = qa_nxt;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (new_row) mfma_s2();           // row block (b+1)/2, after block b used S2
-      if (b == 3) {
-        // no fragment load pending here: wait for the previous step's DMA
-        // and fetch the first packed words of group g+1
-        __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
-        fetch4(pk_next, 0, pw);
-      }
-      if (b == 5) fetch4(pk_next, 1, pw);
-      if (b >= 3) widen_pair(nxt, b - 3);
-      if (b == 6) stage_scale(nxt, pk_next);
+      // keep the row blocks in order: hoisting the scale products of later
+      // row blocks would hold 32 more registers each
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
+  };
+  // Step g: wait for this thread's DMA of group g (the two groups after it
+  // may stay in flight), barrier (every thread's part of group g has landed,
+  // and every wave is done with buffer g - 1), start the DMA of group
+  // g + NBUF - 1 into that freed buffer, compute g.  Past the last group the
+  // DMA fetches the last group again into a buffer nobody reads: every step
+  // then has the same three groups in flight and the loop body no branch.
+  auto step = [&](int g, const Ring& cur, Ring& nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0F76);     // vmcnt(6)
+    __builtin_amdgcn_s_barrier();
+    dma(min(g + NBUF - 1, G - 1), nxt);
     __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
   };
 
-  // prologue: groups 0 and 1 by DMA, group 0 widened into stage 0
-  dma(0, pkb0);
-  dma(G > 1 ? 1 : 0, pkb1);
-  __builtin_amdgcn_s_waitcnt(0x0F73);    // group 0 landed
-  widen_all(stage0, pkb0);
-  stage_scale(stage0, pkb0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("s_barrier" ::: "memory");
-
-  // step for group g reads stage g%2, widens group g+1 (packed buffer
-  // (g+1)%2) into the other stage and DMAs group g+2 into packed buffer g%2;
-  // groups in pairs so that buffers are static
-  group_step(stage0, stage1, pkb1, pkb0, false, G > 2 ? 2 : G - 1);
-  int g = 1;
-  for (; g + 1 < G; g += 2) {
-    group_step(stage1, stage0, pkb0, pkb1, true, g + 2 < G ? g + 2 : G - 1);
-    group_step(stage0, stage1, pkb1, pkb0, true, g + 3 < G ? g + 3 : G - 1);
+  // prologue: groups 0 .. NBUF - 2
+  dma(0, rg0);
+  dma(min(1, G - 1), rg1);
+  dma(min(2, G - 1), rg2);
+  int g = 0;
+  for (; g + NBUF <= G; g += NBUF) {
+    step(g, rg0, rg3);
+    step(g + 1, rg1, rg0);
+    step(g + 2, rg2, rg1);
+    step(g + 3, rg3, rg2);
   }
-  if (g < G) group_step(stage1, stage0, pkb0, pkb1, true, G - 1);
-  fma_block(7);
+  if (g < G) step(g, rg0, rg3);
+  if (g + 1 < G) step(g + 1, rg1, rg0);
+  if (g + 2 < G) step(g + 2, rg2, rg1);
 
   // ------------------------------------------------ epilogue: LR . up^T
   if constexpr (RK > 0) {
@@ -393,13 +295,15 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   // The 32x32 f32 MFMA result has lane l on column l%32, rows
   // 8(e/4) + 4(l/32) + e%4: a direct store writes 2- or 4-byte pieces.  Each
   // wave instead passes one 32-row block row at a time through a private LDS
-  // buffer (the stages are free now) and stores whole 16-byte row pieces.
+  // buffer (the ring is free now: the last step waited for every DMA) and
+  // stores whole 16-byte row pieces.
+  __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): no DMA into the ring in flight
   __syncthreads();
   constexpr int EBYTES = 32 * (WN + 4) * 4;  // one block row of one wave
-  static_assert(4 * EBYTES <= int(sizeof(Stage)), "epilogue buffers must fit in the stages");
-  float* const eb = reinterpret_cast<float*>(
-      wave < 4 ? reinterpret_cast<uint8_t*>(&st0) + wave * EBYTES
-               : reinterpret_cast<uint8_t*>(&st1) + (wave - 4) * EBYTES);
+  static_assert(2 * EBYTES <= int(sizeof(Ring)), "epilogue buffers must fit in the ring");
+  Ring* const eb_ring = wave < 2 ? &rg0 : wave < 4 ? &rg1 : wave < 6 ? &rg2 : &rg3;
+  float* const eb = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(eb_ring) +
+                                             (wave & 1) * EBYTES);
   float bv[CBL];
 #pragma unroll
   for (int j = 0; j < CBL; ++j) {

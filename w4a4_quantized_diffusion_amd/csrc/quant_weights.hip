@@ -217,9 +217,27 @@ __global__ __launch_bounds__(256) void residual_int4_kernel(
     q = q < -8 ? -8 : (q > 7 ? 7 : q);
     nib = q < 0 ? uint32_t(8 | -q) : uint32_t(q);
   }
-  const uint32_t nb = __shfl_down(nib, 1);
+  // the code's 6-bit field of the fold format: |q| in bits 0..2, sign in bit 5
+  const uint32_t field = (nib & 7u) | ((nib & 8u) << 2);
+  // Chunk c (lanes 0..3 write one each) holds the codes k = 8c + j as fields
+  // j and k = 32 + 8c + j as fields 8 + j, j = 0..7: the 96-bit string of
+  // fields 6 bits apart, words o0, o1, o2, is stored as o0 | (o1 & GX),
+  // o2 | (o1 & GY) (the middle word's payload in the outer words' zero
+  // exponent bits).  Every lane gathers; lanes 0..3 store.
+  const int c = lane & 3;
+  uint32_t o[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int f = 0; f < 16; ++f) {
+    const int src = f < 8 ? 8 * c + f : 32 + 8 * c + (f - 8);
+    const uint32_t pf = uint32_t(__shfl(int(field), src));
+    const int bit = 6 * f, w = bit >> 5, sh = bit & 31;
+    o[w] |= pf << sh;
+    if (sh > 26) o[w + 1] |= pf >> (32 - sh);
+  }
   // group-major: wcodes[K/64][N][32 bytes], wscales[K/64][N]
-  if ((lane & 1) == 0) wcodes[(int64_t(g) * N + n) * 32 + lane / 2] = uint8_t(nib | (nb << 4));
+  if (lane < 4)
+    *reinterpret_cast<uint2*>(wcodes + (int64_t(g) * N + n) * 32 + 8 * lane) =
+        make_uint2(o[0] | (o[1] & 0x18618618u), o[2] | (o[1] & 0x61861861u));
   if (lane == 0) wscales[int64_t(g) * N + n] = s;
   if (residual) residual[n * K + k] = R;
 }

@@ -250,9 +250,10 @@ svdq_status linear_w4a4(const void* X, svdq_dtype x_dtype, bool gelu, int64_t M,
                         const uint16_t* lora_down, const uint16_t* lora_up,
                         const uint8_t* wcodes, const void* wscales,
                         const float* w_tensor_scale, const float* x_tensor_scale,
-                        const void* bias, void* Y, svdq_dtype y_dtype, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        const void* bias, svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   TRY(check_dtype(x_dtype, "x_dtype"));
+  if (bias) TRY(check_dtype(bias_dtype, "bias_dtype"));
   if (gelu && x_dtype != SVDQ_BF16)
     return fail(SVDQ_ERR_UNSUPPORTED, "the GELU input form takes bf16 activations");
   TRY(check_prec(prec));
@@ -282,7 +283,7 @@ svdq_status linear_w4a4(const void* X, svdq_dtype x_dtype, bool gelu, int64_t M,
   return svdq_gemm_w4a4(ws + l.codes, ws + l.scales,
                         rank > 0 ? reinterpret_cast<const uint16_t*>(ws + l.lr) : nullptr, M, K,
                         N, rank, prec, wcodes, wscales, lora_up, w_tensor_scale,
-                        x_tensor_scale, bias, x_dtype, Y, y_dtype, stream);
+                        x_tensor_scale, bias, bias_dtype, Y, y_dtype, stream);
 }
 
 }  // namespace
@@ -294,12 +295,12 @@ svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64
                              const uint16_t* lora_down, const uint16_t* lora_up,
                              const uint8_t* wcodes, const void* wscales,
                              const float* w_tensor_scale, const float* x_tensor_scale,
-                             const void* bias, void* Y, svdq_dtype y_dtype, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             const void* bias, svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   svdq::clear_error();
   return linear_w4a4(X, x_dtype, false, M, K, N, rank, prec, smooth, lora_down, lora_up, wcodes,
-                     wscales, w_tensor_scale, x_tensor_scale, bias, Y, y_dtype, workspace,
-                     workspace_bytes, stream);
+                     wscales, w_tensor_scale, x_tensor_scale, bias, bias_dtype, Y, y_dtype,
+                     workspace, workspace_bytes, stream);
 }
 
 svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
@@ -307,13 +308,13 @@ svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, 
                                   const float* smooth, const uint16_t* lora_down,
                                   const uint16_t* lora_up, const uint8_t* wcodes,
                                   const void* wscales, const float* w_tensor_scale,
-                                  const float* x_tensor_scale, const void* bias, void* Y,
-                                  svdq_dtype y_dtype, void* workspace, size_t workspace_bytes,
-                                  hipStream_t stream) {
+                                  const float* x_tensor_scale, const void* bias,
+                                  svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   svdq::clear_error();
   return linear_w4a4(X, x_dtype, true, M, K, N, rank, prec, smooth, lora_down, lora_up, wcodes,
-                     wscales, w_tensor_scale, x_tensor_scale, bias, Y, y_dtype, workspace,
-                     workspace_bytes, stream);
+                     wscales, w_tensor_scale, x_tensor_scale, bias, bias_dtype, Y, y_dtype,
+                     workspace, workspace_bytes, stream);
 }
 
 svdq_status svdq_fold_lora(const uint16_t* lora_down, const uint16_t* lora_up, int64_t N,

@@ -31,7 +31,9 @@ from torch import nn
 from . import svdq
 
 FORMAT = "svdq-w4a4-layers"
-VERSION = 1
+# version 2: INT4 codes in the fold format (include/svdq.h), written by
+# the library's quantizer; version-1 files held textbook nibbles
+VERSION = 2
 
 _SVDQ_FIELDS = ("smooth", "lora_down", "lora_up", "wcodes", "wscales", "w_tensor_scale",
                 "x_tensor_scale")
@@ -55,7 +57,7 @@ def _shapes_awq(n, k, group):
 
 
 class _BiasCache:
-    """The bias in the activations' dtype (the ABI reads it in X's dtype)."""
+    """The bias in bf16 (awq_linear_w4a16 reads a bf16 bias)."""
 
     def __init__(self):
         self.key, self.value = None, None
@@ -74,7 +76,7 @@ class SVDQLinear(nn.Module):
 
     `layer` is a dict as returned by svdq.svdq_quantize_weights or
     svdq.svdq_fold_lora (device tensors plus rank, prec, N, K).  The bias is
-    kept in fp32 and used in the activations' dtype.  With gelu_input the
+    kept in fp32 and added in fp32 by the library.  With gelu_input the
     layer computes Linear(GELU(x)) (tanh GELU fused into the activation pass;
     x must be bf16).  Inputs of any leading shape [..., K] in fp32 or bf16;
     the output has x's dtype.  The workspace is kept between calls and
@@ -99,7 +101,6 @@ class SVDQLinear(nn.Module):
             bias = bias.detach().to(torch.float32).reshape(self.out_features).contiguous()
         self.register_buffer("bias", bias)
         self._ws = None
-        self._bias = _BiasCache()
 
     @classmethod
     def from_linear(cls, linear, act_amax=None, rank=32, prec="int4", gelu_input=False):
@@ -133,8 +134,7 @@ class SVDQLinear(nn.Module):
         if self._ws is None or self._ws.numel() < need or self._ws.device != x2.device:
             self._ws = torch.empty(need, dtype=torch.uint8, device=x2.device)
         fn = svdq.svdq_linear_w4a4_gelu if self.gelu_input else svdq.svdq_linear_w4a4
-        y = fn(x2, self.layer(), self._bias.get(self.bias, x2.dtype), y_dtype=x2.dtype,
-               workspace=self._ws)
+        y = fn(x2, self.layer(), self.bias, y_dtype=x2.dtype, workspace=self._ws)
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self):

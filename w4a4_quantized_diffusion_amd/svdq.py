@@ -40,12 +40,16 @@ _SIG = {
                                                _P, _P, _P, _P, _P, _P, _P]),
     "svdq_gemm_w4a4": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, ctypes.c_int, _P, _P,
                                        _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P]),
+    # X, x_dtype, M, K, N, rank, prec, smooth, lora_down, lora_up, wcodes,
+    # wscales, w_tensor_scale, x_tensor_scale, bias, bias_dtype, Y, y_dtype,
+    # workspace, workspace_bytes, stream
     "svdq_linear_w4a4": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I32, ctypes.c_int,
-                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
-                                         ctypes.c_size_t, _P]),
+                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
+                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "svdq_linear_w4a4_gelu": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I32,
-                                              ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                              ctypes.c_int, _P, ctypes.c_size_t, _P]),
+                                              ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_int, _P, ctypes.c_int, _P, ctypes.c_size_t,
+                                              _P]),
     "svdq_fold_lora": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P, _I32, ctypes.c_float,
                                        _P, _P, _P, _P]),
     "awq_quantize_weights": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
@@ -203,11 +207,12 @@ def svdq_gemm_w4a4(codes, scales, LR, layer, bias=None, y_dtype=torch.float32, Y
 
 def svdq_linear_w4a4(X, layer, bias=None, y_dtype=torch.float32, workspace=None, Y=None,
                      _entry="svdq_linear_w4a4"):
-    """The whole layer.  bias must have X's dtype.  Returns Y [M, N]."""
+    """The whole layer.  bias: float32 or bfloat16 [N] (any of the two,
+    independent of X's dtype) or None.  Returns Y [M, N]."""
     M, K = X.shape
     N, rank, pr = layer["N"], layer["rank"], layer["prec"]
-    if bias is not None and bias.dtype != X.dtype:
-        raise ValueError("bias must have X's dtype")
+    if bias is not None and bias.dtype not in _DT:
+        raise ValueError("bias must be float32 or bfloat16")
     if Y is None:
         Y = _empty((M, N), y_dtype, X.device)
     need = svdq_workspace_bytes(M, K, rank, pr)
@@ -217,8 +222,8 @@ def svdq_linear_w4a4(X, layer, bias=None, y_dtype=torch.float32, workspace=None,
         _p(X), _DT[X.dtype], M, K, N, rank, pr, _p(layer["smooth"]),
         _p(layer["lora_down"]) if rank else None, _p(layer["lora_up"]) if rank else None,
         _p(layer["wcodes"]), _p(layer["wscales"]), _p(layer["w_tensor_scale"]),
-        _p(layer["x_tensor_scale"]), _p(bias), _p(Y), _DT[Y.dtype], _p(workspace),
-        workspace.numel(), _stream()))
+        _p(layer["x_tensor_scale"]), _p(bias), _DT[bias.dtype] if bias is not None else F32,
+        _p(Y), _DT[Y.dtype], _p(workspace), workspace.numel(), _stream()))
     return Y
 
 
