@@ -198,6 +198,30 @@ svdq_status svdq_linear_w4a4(const void* X, svdq_dtype x_dtype, int64_t M, int64
                              svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * layer as svdq_linear_w4a4, with its workspace in a fixed scratch array that
+ * the library holds on each GPU it runs on (32 MiB, kept until the process
+ * ends) instead of a caller-provided buffer.  It allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.  The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress).
+ * Arguments, layouts and errors as svdq_linear_w4a4; a layer whose workspace
+ * (svdq_workspace_bytes) exceeds svdq_noalloc_max_workspace_bytes() returns
+ * SVDQ_ERR_INVALID_ARG before any HIP call (e.g. INT4, rank 32: K 3072 up to
+ * M 9216 rows; K 12288 up to M 4608 rows).  Every call on one GPU shares its
+ * array: calls that overlap in time on one GPU (concurrent streams) race and
+ * give undefined results; calls ordered on one stream, or otherwise
+ * serialized, are correct.  Nothing in the array needs to start at zero. */
+size_t svdq_noalloc_max_workspace_bytes(void);
+svdq_status svdq_linear_w4a4_noalloc(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                                     int64_t N, int32_t rank, svdq_precision prec,
+                                     const float* smooth, const uint16_t* lora_down,
+                                     const uint16_t* lora_up, const uint8_t* wcodes,
+                                     const void* wscales, const float* w_tensor_scale,
+                                     const float* x_tensor_scale, const void* bias,
+                                     svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                                     hipStream_t stream);
+
 /* The MLP down-projection's input form: the same calls with X replaced by
  * GELU(X), fused into the activation pass (the original engine's fused
  * GELU / MLP kernels: chaosnode.de page, "Nunchaku Lite vs. Original").

@@ -187,3 +187,21 @@ def test_fold_lora_validation(lib):
              ctypes.byref(r), None) == INVALID
     assert "overlap" in svdq.svdq_last_error()
     assert r.value == -1
+
+
+def test_noalloc_rejects_workspace_beyond_the_scratch(lib):
+    """The entry point that allocates nothing checks the workspace size against
+    its fixed scratch before any HIP call (fake pointers are never touched)."""
+    p = ctypes.c_void_p
+    cap = lib.svdq_noalloc_max_workspace_bytes()
+    assert cap == 32 << 20
+    # INT4, K 12288, rank 32: 4608 rows fit, 9216 do not
+    assert svdq.svdq_workspace_bytes(4608, 12288, 32, "int4") <= cap
+    assert svdq.svdq_workspace_bytes(9216, 12288, 32, "int4") > cap
+    st = lib.svdq_linear_w4a4_noalloc(p(0x10000), 1, 9216, 12288, 64, 32, 0, p(0x20000),
+                                      p(0x30000), p(0x40000), p(0x50000), p(0x60000), None,
+                                      None, None, 0, p(0x70000), 1, None)
+    assert st == INVALID and "scratch" in svdq.svdq_last_error()
+    # M == 0 launches nothing and needs no device
+    assert lib.svdq_linear_w4a4_noalloc(None, 1, 0, 128, 64, 16, 0, *([None] * 8), 0, None, 1,
+                                        None) == 0

@@ -4,6 +4,7 @@
 #include "internal.h"
 
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 namespace svdq {
@@ -315,6 +316,78 @@ svdq_status svdq_linear_w4a4_gelu(const void* X, svdq_dtype x_dtype, int64_t M, 
   return linear_w4a4(X, x_dtype, true, M, K, N, rank, prec, smooth, lora_down, lora_up, wcodes,
                      wscales, w_tensor_scale, x_tensor_scale, bias, bias_dtype, Y, y_dtype,
                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------- no allocation
+// The workspace of svdq_linear_w4a4_noalloc: a fixed device array (each GPU
+// the library runs on holds its own copy until the process ends).  Its name
+// is only a host-side stand-in; host code uses the device address that
+// hipGetSymbolAddress returns for the current device.
+namespace {
+
+constexpr size_t SCRATCH_BYTES = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// the scratch array's address on the current device, looked up once per device
+svdq_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  SVDQ_CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(SVDQ_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    SVDQ_CHECK_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(SVDQ_ERR_HIP, "hipGetSymbolAddress returned no address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t svdq_noalloc_max_workspace_bytes(void) { return SCRATCH_BYTES; }
+
+svdq_status svdq_linear_w4a4_noalloc(const void* X, svdq_dtype x_dtype, int64_t M, int64_t K,
+                                     int64_t N, int32_t rank, svdq_precision prec,
+                                     const float* smooth, const uint16_t* lora_down,
+                                     const uint16_t* lora_up, const uint8_t* wcodes,
+                                     const void* wscales, const float* w_tensor_scale,
+                                     const float* x_tensor_scale, const void* bias,
+                                     svdq_dtype bias_dtype, void* Y, svdq_dtype y_dtype,
+                                     hipStream_t stream) {
+  svdq::clear_error();
+  TRY(check_prec(prec));
+  TRY(check_mkr(M, K, rank));
+  if (M == 0) return SVDQ_OK;
+  const size_t need = layout(M, K, rank, prec).total;
+  if (need > SCRATCH_BYTES)
+    return fail(SVDQ_ERR_INVALID_ARG, "the workspace of M=" + std::to_string(M) + ", K=" +
+                                          std::to_string(K) + ", rank=" + std::to_string(rank) +
+                                          " needs " + std::to_string(need) +
+                                          " bytes, above the fixed scratch of " +
+                                          std::to_string(SCRATCH_BYTES) + " bytes");
+  // the usual argument checks of the layer before the first HIP call
+  TRY(check_dtype(x_dtype, "x_dtype"));
+  TRY(check_dtype(y_dtype, "y_dtype"));
+  if (bias) TRY(check_dtype(bias_dtype, "bias_dtype"));
+  if (N <= 0 || N > MAX_DIM || N % 16 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "N must be a positive multiple of 16");
+  TRY(check_ptr(X, "X"));
+  TRY(check_ptr(Y, "Y"));
+  void* ws = nullptr;
+  TRY(scratch_on_current_device(&ws));
+  return linear_w4a4(X, x_dtype, false, M, K, N, rank, prec, smooth, lora_down, lora_up, wcodes,
+                     wscales, w_tensor_scale, x_tensor_scale, bias, bias_dtype, Y, y_dtype, ws,
+                     SCRATCH_BYTES, stream);
 }
 
 svdq_status svdq_fold_lora(const uint16_t* lora_down, const uint16_t* lora_up, int64_t N,

@@ -50,6 +50,10 @@ _SIG = {
                                               ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_int, _P, ctypes.c_int, _P, ctypes.c_size_t,
                                               _P]),
+    "svdq_noalloc_max_workspace_bytes": (ctypes.c_size_t, []),
+    "svdq_linear_w4a4_noalloc": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I32,
+                                                 ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                 ctypes.c_int, _P, ctypes.c_int, _P]),
     "svdq_fold_lora": (ctypes.c_int, [_P, _P, _I64, _I64, _I32, _P, _P, _I32, ctypes.c_float,
                                        _P, _P, _P, _P]),
     "awq_quantize_weights": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
@@ -224,6 +228,29 @@ def svdq_linear_w4a4(X, layer, bias=None, y_dtype=torch.float32, workspace=None,
         _p(layer["wcodes"]), _p(layer["wscales"]), _p(layer["w_tensor_scale"]),
         _p(layer["x_tensor_scale"]), _p(bias), _DT[bias.dtype] if bias is not None else F32,
         _p(Y), _DT[Y.dtype], _p(workspace), workspace.numel(), _stream()))
+    return Y
+
+
+def svdq_noalloc_max_workspace_bytes():
+    return int(lib().svdq_noalloc_max_workspace_bytes())
+
+
+def svdq_linear_w4a4_noalloc(X, layer, bias=None, y_dtype=torch.float32, Y=None):
+    """The whole layer with the library's fixed device scratch as workspace
+    (no allocation by the library; Y is allocated here only when not given).
+    Calls that overlap on one GPU race on the shared scratch."""
+    M, K = X.shape
+    N, rank, pr = layer["N"], layer["rank"], layer["prec"]
+    if bias is not None and bias.dtype not in _DT:
+        raise ValueError("bias must be float32 or bfloat16")
+    if Y is None:
+        Y = _empty((M, N), y_dtype, X.device)
+    _check(lib().svdq_linear_w4a4_noalloc(
+        _p(X), _DT[X.dtype], M, K, N, rank, pr, _p(layer["smooth"]),
+        _p(layer["lora_down"]) if rank else None, _p(layer["lora_up"]) if rank else None,
+        _p(layer["wcodes"]), _p(layer["wscales"]), _p(layer["w_tensor_scale"]),
+        _p(layer["x_tensor_scale"]), _p(bias), _DT[bias.dtype] if bias is not None else F32,
+        _p(Y), _DT[Y.dtype], _stream()))
     return Y
 
 
