@@ -89,11 +89,9 @@ def test_awq_linear_ragged(m, k, n):
     _check_linear(m, k, n, seed=2, ybf16=False)
 
 
-def test_awq_linear_full_size_sampled_rows():
-    """M 4608, K 3072, N 12288: Y on sampled rows (first and last included)."""
-    m = 4608
-    rows = np.concatenate([np.random.default_rng(3).choice(m, 16, replace=False), [0, m - 1]])
-    _check_linear(m, 3072, 12288, seed=0, rows=rows, ybf16=True)
+def test_awq_linear_full_size_all_rows():
+    """M 4608, K 3072, N 12288: Y within tolerance on every row."""
+    _check_linear(4608, 3072, 12288, seed=0, ybf16=True)
 
 
 @pytest.mark.parametrize("m", [16, 200])

@@ -4,10 +4,14 @@ activation pass applies GELU to its bf16 input first) against the oracle.
 The fused step rounds an fp32 GELU value to bf16.  Where the float64 GELU lies
 within a few fp32 ulps of a bf16 rounding midpoint, fp32 evaluation may round
 either way; both results are correct.  Those elements are found from the
-oracle's float64 values alone, and the quantization groups (INT4: 64 along
-K, NVFP4 blocks of 16) that contain one are left out of the bit-exact
-comparison, which covers all the others.  Y is compared within the layer
-tolerance everywhere."""
+oracle's float64 values alone.  Quantization groups (INT4: 64 along K, NVFP4
+blocks of 16) without one are compared bit for bit with the oracle; a group
+holding some must equal, bit for bit, the oracle's quantization of one of
+the admissible inputs, where each ambiguous element takes either of its two
+neighbouring bf16 values.  Y is compared within the layer tolerance
+everywhere."""
+
+import itertools
 
 import numpy as np
 import pytest
@@ -34,6 +38,31 @@ def ambiguous(x):
     margin = 8 + 16 * np.minimum(np.abs(u), 10.0)
     low = (g32.view(np.uint32) & 0xFFFF).astype(np.float64)
     return np.abs(low - 0x8000) <= margin
+
+
+def neighbours(x):
+    """The two bf16 values around the fp32 GELU value of each element (the
+    candidates where it lies near their midpoint): truncation of the fp32
+    bits and the next bf16 value away from zero."""
+    g32 = F.fl32(O.gelu_tanh(np.asarray(x, dtype=np.float64))).astype(np.float32)
+    lo = (g32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    hi = ((g32.view(np.uint32) & np.uint32(0xFFFF0000)) + np.uint32(0x10000)).view(np.float32)
+    return lo, hi
+
+
+def admissible(xg_row, lo, hi, idx, quantize, got, max_enum=12):
+    """Whether `got` (the GPU's bytes for one group) equals quantize(v) for
+    some admissible input v: xg_row with each element of idx replaced by its
+    lo or hi neighbour.  Groups with more than max_enum ambiguous elements
+    (none at these sizes) are checked with the first max_enum enumerated and
+    the rest at the oracle's choice."""
+    idx = np.asarray(idx)[:max_enum]
+    for combo in itertools.product((False, True), repeat=len(idx)):
+        v = xg_row.copy()
+        v[idx] = np.where(combo, hi[idx], lo[idx])
+        if quantize(v) == got:
+            return True
+    return False
 
 
 def group_mask(amb, width):
@@ -72,6 +101,20 @@ def _int4_check(x, lay, rank):
     assert np.array_equal(got_c[keep], ref_c[keep]), "codes differ outside ambiguous groups"
     got_s = scales.cpu().numpy().T.view(np.uint32)
     assert np.array_equal(got_s[keep], sa.view(np.uint32)[keep]), "scales differ"
+    # every ambiguous group: the GPU's scale and codes are the oracle's for
+    # some admissible choice of its ambiguous elements
+    lo, hi = neighbours(x)
+    smooth = np.asarray(lay["smooth"], dtype=np.float32)
+
+    def q_int4(v, g):
+        q, sc = O.quantize_activations(v[None, :], smooth[64 * g:64 * g + 64])
+        return O.pack_int4(q).tobytes() + sc.view(np.uint32).tobytes()
+
+    for r, g in zip(*np.nonzero(gm)):
+        sl = slice(64 * g, 64 * g + 64)
+        got = got_c[r, g].tobytes() + got_s[r, g].tobytes()
+        assert admissible(xg[r, sl].copy(), lo[r, sl], hi[r, sl], np.nonzero(amb[r, sl])[0],
+                          lambda v: q_int4(v, g), got), f"row {r} group {g}: not admissible"
     if rank:
         lr_check(lr, xg, lay["lora_down"], amb)
     return gm.sum()
@@ -120,6 +163,19 @@ def test_act_quantize_gelu_nvfp4():
     assert np.array_equal(got_c[keep_bytes], ref_c[keep_bytes]), "E2M1 codes differ"
     got_s = scales.cpu().numpy().transpose(1, 0, 2).reshape(m, k // 16)
     assert np.array_equal(got_s[~gm], sb[~gm]), "E4M3 block scales differ"
+    # every ambiguous block: admissible (see the module docstring)
+    lo, hi = neighbours(x)
+    smooth = np.asarray(lay["smooth"], dtype=np.float32)
+
+    def q_fp4(v, b):
+        e1, sb1 = O4.quantize_activations(v[None, :], smooth[16 * b:16 * b + 16], ts_x)
+        return O.pack_nibbles(e1).tobytes() + sb1.tobytes()
+
+    for r, b in zip(*np.nonzero(gm)):
+        sl = slice(16 * b, 16 * b + 16)
+        got = got_c[r, 8 * b:8 * b + 8].tobytes() + got_s[r, b:b + 1].tobytes()
+        assert admissible(xg[r, sl].copy(), lo[r, sl], hi[r, sl], np.nonzero(amb[r, sl])[0],
+                          lambda v: q_fp4(v, b), got), f"row {r} block {b}: not admissible"
     lr_check(lr, xg, lay["lora_down"], amb)
 
 

@@ -230,11 +230,36 @@ def test_quantize_weights_svd_quality():
     assert np.all(np.abs(r - sw * q) <= 0.5 * sw * (1 + 2 ** -22))
 
 
+@pytest.mark.parametrize("n,k", [(12288, 3072), (3072, 12288)])
+def test_quantize_weights_svd_quality_flux_shapes(n, k):
+    """The library's SVD at the FLUX projection shapes, rank 32: the
+    Frobenius error of its (bf16) rank-32 part of the smoothed weight is
+    within 0.2% of the Eckart-Young optimum sum_{i>32} sigma_i^2 (LAPACK
+    singular values, float64), plus the bf16 rounding of the factors
+    (2^-16 of the energy of the top 32)."""
+    rank = 32
+    s = synth.layer(256, k, n, rank, seed=4, workload="flagship")
+    amax = O.act_absmax(s["x"])
+    out = svdq.svdq_quantize_weights(t_f32(s["w"]), t_f32(amax), rank, "int4")
+    torch.cuda.synchronize()
+    lam, _ = O.smoothing(amax, s["w"])
+    lam64 = lam.astype(np.float64)
+    wh = s["w"].astype(np.float64) * lam64[None, :]
+    sv = np.linalg.svd(wh, compute_uv=False)
+    ey = np.sum(sv[rank:] ** 2)
+    top = np.sum(sv[:rank] ** 2)
+    down = F.bf16_to_f32(bf16_bits_np(out["lora_down"])).astype(np.float64)
+    up = F.bf16_to_f32(bf16_bits_np(out["lora_up"])).astype(np.float64)
+    err = np.sum((wh - lam64[None, :] * (up @ down)) ** 2)
+    assert err <= ey * (1 + 2e-3) + 2.0 ** -16 * top, (err / ey, ey, top)
+
+
 # ------------------------------------------------------------ full size
 
-def test_flagship_full_size_sampled_rows():
+def test_flagship_full_size_all_rows():
     """M 4096, K 3072, N 12288, rank 32 (the benchmark's configuration):
-    activation codes / scales bit-exact on every row, Y on sampled rows."""
+    activation codes / scales bit-exact and Y, LR within tolerance on every
+    row (every wave and row-block position of every tile)."""
     m, k, n, rank = 4096, 3072, 12288, 32
     x = synth.layer(m, k, 16, 0, seed=0)["x"]
     lay = random_int4_layer(n, k, rank, seed=0)
@@ -248,20 +273,18 @@ def test_flagship_full_size_sampled_rows():
     qx, sa = O.quantize_activations(x, lay["smooth"])
     assert np.array_equal(rm_int4(codes.cpu().numpy()), O.pack_int4(qx))
     assert np.array_equal(scales.cpu().numpy().T, sa)
-    rows = np.random.default_rng(0).choice(m, 24, replace=False)
-    rows = np.concatenate([rows, [0, m - 1]])
-    y_ref, _ = O.linear_w4a4(x[rows], lay)
-    assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, "flagship rows")
-    assert_lr_close(lr[torch.from_numpy(rows).cuda()], x[rows], lay["lora_down"], "flagship LR")
+    y_ref, _ = O.linear_w4a4(x, lay)
+    assert_y_close(y, y_ref, True, "flagship, all rows")
+    assert_lr_close(lr, x, lay["lora_down"], "flagship LR")
 
 
 @pytest.mark.parametrize("m,k,n,workload", [(4608, 3072, 9216, "attn"), (4608, 3072, 3072, "attn"),
                                             (4608, 12288, 3072, "mlp"), (9216, 3072, 12288, "mlp")])
-def test_dit_shapes_full_size_sampled_rows(m, k, n, workload):
+def test_dit_shapes_full_size_all_rows(m, k, n, workload):
     """The DiT projection shapes at rank 32: attention QKV and output
     projections at 4608 tokens, the MLP down-projection (K 12288), the MLP
-    up-projection at batch 2 (M 9216).  Activation codes / scales bit-exact on
-    every row, Y and LR on sampled rows (first and last included)."""
+    up-projection at batch 2 (M 9216).  Activation codes / scales bit-exact,
+    Y and LR within tolerance, on every row."""
     rank = 32
     x = synth.layer(m, k, 16, 0, seed=2, workload=workload)["x"]
     lay = random_int4_layer(n, k, rank, seed=2, workload=workload)
@@ -273,11 +296,9 @@ def test_dit_shapes_full_size_sampled_rows(m, k, n, workload):
     qx, sa = O.quantize_activations(x, lay["smooth"])
     assert np.array_equal(rm_int4(codes.cpu().numpy()), O.pack_int4(qx))
     assert np.array_equal(scales.cpu().numpy().T, sa)
-    rows = np.random.default_rng(1).choice(m, 16, replace=False)
-    rows = np.concatenate([rows, [0, m - 1]])
-    y_ref, _ = O.linear_w4a4(x[rows], lay)
-    assert_y_close(y[torch.from_numpy(rows).cuda()], y_ref, True, f"{workload} M{m} K{k} N{n} rows")
-    assert_lr_close(lr[torch.from_numpy(rows).cuda()], x[rows], lay["lora_down"], "LR")
+    y_ref, _ = O.linear_w4a4(x, lay)
+    assert_y_close(y, y_ref, True, f"{workload} M{m} K{k} N{n}, all rows")
+    assert_lr_close(lr, x, lay["lora_down"], "LR")
 
 
 def test_linear_graph_replay_matches_eager():

@@ -46,3 +46,34 @@ def test_gelu_input_is_bf16_of_fp32_value():
     step = np.where(ref != 0, 2.0 ** (np.floor(np.log2(np.abs(ref) + 1e-300)) - 7), 0)
     assert np.all(np.abs(g - ref) <= 0.5 * step * (1 + 2 ** -15) + 1e-45)
     assert np.array_equal(F.bf16_bits(F.fl32(ref)), (bits >> 16).astype(np.uint16))
+
+
+def test_admissible_group_check():
+    """The GPU GELU test's check for groups holding an element near a bf16
+    midpoint: it accepts the quantization of either neighbour of that element
+    and rejects a group whose codes match neither."""
+    from tests.test_gpu_gelu import admissible, ambiguous, neighbours
+    rng = np.random.default_rng(3)
+    x = rng.normal(0.0, 2.0, 200000).astype(np.float32)
+    amb = ambiguous(x)
+    k = int(np.nonzero(amb)[0][0])
+    row = rng.normal(0.0, 1.0, 64).astype(np.float32)
+    row[5] = x[k]                                    # one ambiguous element in the group
+    assert ambiguous(row)[5]
+    xg = O.gelu_input(row)
+    lo, hi = neighbours(row)
+    assert lo[5] != hi[5] and xg[5] in (lo[5], hi[5])
+    smooth = np.ones(64, np.float32)
+
+    def q(v):
+        c, s = O.quantize_activations(v[None, :], smooth)
+        return O.pack_int4(c).tobytes() + s.view(np.uint32).tobytes()
+
+    idx = np.nonzero(ambiguous(row))[0]
+    for pick in (lo, hi):
+        v = xg.copy()
+        v[idx] = pick[idx]
+        assert admissible(xg.copy(), lo, hi, idx, q, q(v))
+    bad = bytearray(q(xg))
+    bad[0] ^= 0x01                                   # a code no choice gives
+    assert not admissible(xg.copy(), lo, hi, idx, q, bytes(bad))

@@ -224,6 +224,42 @@ def test_forward_on_grid_reduces_to_matmul():
     assert np.array_equal(aux["qx"], qa)
 
 
+def test_forward_with_power_of_two_smoothing_is_exact():
+    """Non-trivial smoothing pinned: calibration statistics chosen so that
+    lam_k = 2^e_k exactly (e_k in -3..3), X = Xh_grid diag(lam) and
+    W = Wh_grid diag(lam)^-1 with Xh_grid, Wh_grid on the INT4 grid (a code 7
+    in every group, power-of-two group scales).  Smoothing must give back
+    Xh_grid and Wh_grid exactly, so the layer is lossless: its codes are the
+    grid codes and Y equals the float64 matmul X W^T + b.  Skipping the
+    smoothing, or applying lam instead of 1/lam to X, moves X off the grid."""
+    g = np.random.default_rng(13)
+    m, k, n = 7, 192, 11
+    qa = g.integers(-7, 8, (m, k)); qa[:, 5::64] = 7
+    qb = g.integers(-7, 8, (n, k)); qb[:, 40::64] = -7
+    ea = np.ldexp(1.0, g.integers(-5, 3, (m, k // 64)))
+    eb = np.ldexp(1.0, g.integers(-8, -3, (n, k // 64)))
+    e = g.integers(-3, 4, k)
+    lam = np.ldexp(1.0, e)
+    xh = (qa.reshape(m, 3, 64) * ea[:, :, None]).reshape(m, k)
+    wh = (qb.reshape(n, 3, 64) * eb[:, :, None]).reshape(n, k)
+    x = (xh * lam[None, :]).astype(np.float32)
+    w = (wh / lam[None, :]).astype(np.float32)
+    amax_w = np.max(np.abs(w), axis=0).astype(np.float32)
+    amax_x = (amax_w.astype(np.float64) * np.ldexp(1.0, 2 * e)).astype(np.float32)
+    l2, sm = svdq.smoothing(amax_x, w)
+    assert np.array_equal(l2, lam.astype(np.float32)) and np.array_equal(sm, (1 / lam).astype(np.float32))
+    layer = svdq.quantize_weights(w, amax_x, 0)
+    assert np.array_equal(layer["R"], wh.astype(np.float32))
+    assert np.array_equal(svdq.smooth_activations(x, layer["smooth"]), xh)
+    b = g.standard_normal(n).astype(np.float32)
+    y, aux = svdq.linear_w4a4(x, layer, b)
+    assert np.array_equal(aux["qx"], qa)
+    assert np.array_equal(y, x.astype(np.float64) @ w.astype(np.float64).T + b)
+    # the same inputs without smoothing are off the grid: lossy
+    y0, aux0 = svdq.linear_w4a4(x, dict(layer, smooth=np.ones(k, np.float32)), b)
+    assert not np.array_equal(aux0["qx"], qa)
+
+
 def test_forward_zero_residual_is_exact():
     """W exactly equal to a bf16 low-rank product (small integers): R == 0,
     every weight code is 0, and the layer returns X W^T + b exactly."""
