@@ -193,39 +193,52 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   // takes rows from lanes 32 b + r and columns from lanes 32 b + c for block
   // b: every lane passes its row's sA and the sW of column l of the wave
   // tile), then per column block the exact integer products I_g and one FMA
-  // per element, acc += S (.) I.
+  // per element, acc += S (.) I.  The last row block's FMAs wait for the next
+  // group: they run right after its barrier, while the LDS reads of its first
+  // operands are in flight (the group before the first one has S = P = 0).
+  v32f S = zero32;
+  v16f P[CBL];
+#pragma unroll
+  for (int j = 0; j < CBL; ++j) P[j] = zero;
+  auto fmas = [&](int i) {
+    // the FMAs issue at raised wave priority: of the two waves on a SIMD,
+    // the one with vector work ready goes first and the other's MFMA issue
+    // slips behind it, so the pair drifts out of step
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int j = 0; j < CBL; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(S[16 * j + e], P[j][e], acc[i][j][e]);
+    __builtin_amdgcn_s_setprio(0);
+  };
   auto compute = [&](const Ring& cur) {
+    uint4 rb_raw[CBL];
+#pragma unroll
+    for (int j = 0; j < CBL; ++j) rb_raw[j] = cur.code[boff + 64 * j];
+    const float qb = cur.scale[BM + wn * WN + lane];
+    uint4 fa_raw = cur.code[aoff];
+    float qa = cur.scale[wm * WM + r32];
+    fmas(RBL - 1);
     v8i fb[CBL];
 #pragma unroll
-    for (int j = 0; j < CBL; ++j) fb[j] = decode_frag(cur.code[boff + 64 * j]);
-    const float qb = cur.scale[BM + wn * WN + lane];
-    v8i fa = decode_frag(cur.code[aoff]);
-    float qa = cur.scale[wm * WM + r32];
+    for (int j = 0; j < CBL; ++j) fb[j] = decode_frag(rb_raw[j]);
+    v8i fa = decode_frag(fa_raw);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < RBL; ++i) {
       // the next row block's packed fragment and scale load while this one runs
-      uint4 fa_raw;
       float qa_nxt;
       if (i + 1 < RBL) {
         fa_raw = cur.code[aoff + 64 * (i + 1)];
         qa_nxt = cur.scale[wm * WM + (i + 1) * 32 + r32];
       }
-      const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(qa, qb, zero32, 0, 0, 0);
-      v16f P[CBL];
+      S = __builtin_amdgcn_mfma_f32_32x32x1f32(qa, qb, zero32, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < CBL; ++j)
         P[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             fa, fb[j], zero, FMT_FP6, FMT_FP6, 0, CODE_SCALE, 0, CODE_SCALE);
-      // the FMAs issue at raised wave priority: of the two waves on a SIMD,
-      // the one with vector work ready goes first and the other's MFMA issue
-      // slips behind it, so the pair drifts out of step
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int j = 0; j < CBL; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(S[16 * j + e], P[j][e], acc[i][j][e]);
-      __builtin_amdgcn_s_setprio(0);
       if (i + 1 < RBL) {
+        fmas(i);
         fa = decode_frag(fa_raw);
         qa = qa_nxt;
       }
@@ -262,6 +275,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   if (g < G) step(g, rg0, rg3);
   if (g + 1 < G) step(g + 1, rg1, rg0);
   if (g + 2 < G) step(g + 2, rg2, rg1);
+  fmas(RBL - 1);
 
   // ------------------------------------------------ epilogue: LR . up^T
   if constexpr (RK > 0) {
