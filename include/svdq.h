@@ -35,6 +35,10 @@
  *    SVDQ_ERR_INVALID_ARG (nothing is launched), an unsupported combination
  *    SVDQ_ERR_UNSUPPORTED, a HIP runtime error SVDQ_ERR_HIP.  No call aborts
  *    or throws.  svdq_last_error() gives a message for the calling thread.
+ *  - Size limits: M, N and K at most 2^30, M * K at most 2^40, and for the
+ *    calls that run a GEMM (svdq_gemm_w4a4, svdq_linear_w4a4*,
+ *    awq_linear_w4a16) at most 2^31 - 1 output tiles of 256 x 256
+ *    (ceil(M / 256) * ceil(N / 256)); beyond them SVDQ_ERR_INVALID_ARG.
  *  - Results are deterministic: identical inputs give identical bits.
  *  - Inputs with NaN or Inf are outside the contract (the output is then
  *    unspecified, but every kernel still terminates).

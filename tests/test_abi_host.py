@@ -205,3 +205,42 @@ def test_noalloc_rejects_workspace_beyond_the_scratch(lib):
     # M == 0 launches nothing and needs no device
     assert lib.svdq_linear_w4a4_noalloc(None, 1, 0, 128, 64, 16, 0, *([None] * 8), 0, None, 1,
                                         None) == 0
+
+
+def test_gemm_calls_reject_too_many_output_tiles(lib):
+    """M x N beyond 2^31 - 1 tiles of 256 x 256 (the GEMMs index tiles with
+    32-bit integers) is rejected before any HIP call (fake pointers are never
+    touched); the largest legal M and N alone pass the size checks."""
+    p = ctypes.c_void_p
+    big = 1 << 30
+    st = lib.svdq_gemm_w4a4(p(0x10000), p(0x20000), None, big, 64, big, 0, 0, p(0x30000),
+                            p(0x40000), None, None, None, None, 0, p(0x50000), 1, None)
+    assert st == INVALID and "tiles" in svdq.svdq_last_error()
+    st = lib.svdq_linear_w4a4(p(0x10000), 1, big, 64, big, 0, 0, p(0x20000), None, None,
+                              p(0x40000), p(0x50000), None, None, None, 0, p(0x70000), 1,
+                              p(0x100000), 1 << 40, None)
+    assert st == INVALID and "tiles" in svdq.svdq_last_error()
+    st = lib.awq_linear_w4a16(p(0x10000), big, 64, big, 64, p(0x20000), p(0x30000),
+                              p(0x40000), None, p(0x50000), 1, None)
+    assert st == INVALID and "tiles" in svdq.svdq_last_error()
+    # over 2^30 rows or columns: out of range
+    st = lib.svdq_gemm_w4a4(p(0x10000), p(0x20000), None, big + 1, 64, 64, 0, 0, p(0x30000),
+                            p(0x40000), None, None, None, None, 0, p(0x50000), 1, None)
+    assert st == INVALID
+
+
+def test_fold_lora_binding_rejects_wrong_dtype_and_device():
+    """The binding checks the adapter before calling the library: an fp32 or
+    fp16 adapter (whose bytes the kernel would read as bf16 bit patterns) and
+    an adapter on another device than the layer are rejected."""
+    import torch
+    layer = {"N": 32, "K": 64, "rank": 0, "wcodes": torch.zeros(1, 32, 32, dtype=torch.uint8)}
+    a = torch.zeros(4, 64, dtype=torch.bfloat16)
+    b = torch.zeros(32, 4, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        svdq.svdq_fold_lora(layer, a.float(), b)
+    with pytest.raises(TypeError):
+        svdq.svdq_fold_lora(layer, a, b.half())
+    layer_meta = dict(layer, wcodes=torch.zeros(1, 32, 32, dtype=torch.uint8, device="meta"))
+    with pytest.raises(ValueError):
+        svdq.svdq_fold_lora(layer_meta, a, b)

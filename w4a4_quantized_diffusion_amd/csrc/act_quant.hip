@@ -80,13 +80,25 @@ __device__ __forceinline__ void load_down(const uint16_t* __restrict__ down, int
   }
 }
 
+// The tile is the wave's own: lanes write it here and other lanes of the same
+// wave read it as an MFMA operand.  Wavefront-scope fences around a wave
+// barrier order the previous step's reads before these writes, and these
+// writes before this step's reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int RB, bool PRE>
 __device__ __forceinline__ void stage_down(uint8_t* tile, int lane, const DownRaw<RB, PRE>& d) {
   if constexpr (RB > 0 && PRE) {
+    wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < 2 * RB; ++i)
       *reinterpret_cast<v4i*>(tile + ((lane >> 3) + 8 * i) * DOWN_ROW + (lane & 7) * 16) =
           v4i{int(d.v[i].x), int(d.v[i].y), int(d.v[i].z), int(d.v[i].w)};
+    wave_lds_sync();
   }
 }
 

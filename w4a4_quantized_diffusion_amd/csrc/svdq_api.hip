@@ -64,6 +64,15 @@ svdq_status check_mkr(int64_t M, int64_t K, int32_t rank) {
   return SVDQ_OK;
 }
 
+// The GEMM kernels cover Y with 256 x 256 tiles, one workgroup each, and
+// index tiles with 32-bit integers.
+svdq_status check_tiles(int64_t M, int64_t N) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles > int64_t(INT32_MAX))
+    return fail(SVDQ_ERR_INVALID_ARG, "M x N too large: more than 2^31 - 1 output tiles of 256 x 256");
+  return SVDQ_OK;
+}
+
 #define TRY(x)                            \
   do {                                    \
     svdq_status st_ = (x);                \
@@ -218,6 +227,7 @@ svdq_status svdq_gemm_w4a4(const uint8_t* codes, const void* scales, const uint1
   if (bias) TRY(check_dtype(bias_dtype, "bias_dtype"));
   if (N <= 0 || N > MAX_DIM || N % 16 != 0)
     return fail(SVDQ_ERR_INVALID_ARG, "N must be a positive multiple of 16");
+  TRY(check_tiles(M, N));
   if (M == 0) return SVDQ_OK;
   TRY(check_ptr(codes, "codes"));
   TRY(check_ptr(scales, "scales", 4));
@@ -261,6 +271,7 @@ svdq_status linear_w4a4(const void* X, svdq_dtype x_dtype, bool gelu, int64_t M,
   TRY(check_mkr(M, K, rank));
   if (N <= 0 || N > MAX_DIM || N % 16 != 0)
     return fail(SVDQ_ERR_INVALID_ARG, "N must be a positive multiple of 16");
+  TRY(check_tiles(M, N));
   if (M == 0) return SVDQ_OK;
   const Layout l = layout(M, K, rank, prec);
   TRY(check_ptr(workspace, "workspace", 256));
@@ -460,6 +471,7 @@ svdq_status awq_linear_w4a16(const uint16_t* X, int64_t M, int64_t K, int64_t N,
     return fail(SVDQ_ERR_INVALID_ARG, "K must be a positive multiple of 64");
   if (N <= 0 || N > MAX_DIM || N % 16 != 0)
     return fail(SVDQ_ERR_INVALID_ARG, "N must be a positive multiple of 16");
+  TRY(check_tiles(M, N));
   if (M == 0) return SVDQ_OK;
   TRY(check_ptr(X, "X"));
   TRY(check_ptr(q, "q"));

@@ -270,6 +270,13 @@ def svdq_fold_lora(layer, A, B, scale=1.0):
     patterns): rank becomes round_up(rank + r_lora, 16), lora_down / lora_up
     are new tensors, every other entry is shared with `layer`."""
     N, K, rank = layer["N"], layer["K"], layer["rank"]
+    for name, t in (("A", A), ("B", B)):
+        if t.dtype not in (torch.bfloat16, torch.int16):
+            raise TypeError(f"{name} must be bfloat16 (or its int16 bit patterns), got {t.dtype}")
+        if t.device != layer["wcodes"].device:
+            raise ValueError(f"{name} is on {t.device}, the layer on {layer['wcodes'].device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
     A, B = _bf16_bits(A), _bf16_bits(B)
     r_lora = A.shape[0]
     if A.dim() != 2 or A.shape[1] != K or B.dim() != 2 or tuple(B.shape) != (N, r_lora):
