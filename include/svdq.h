@@ -35,7 +35,7 @@
  *    SVDQ_ERR_INVALID_ARG (nothing is launched), an unsupported combination
  *    SVDQ_ERR_UNSUPPORTED, a HIP runtime error SVDQ_ERR_HIP.  No call aborts
  *    or throws.  svdq_last_error() gives a message for the calling thread.
- *  - Size limits: M, N and K at most 2^30, M * K at most 2^40, and for the
+ *  - Size limits: M, N and K at most 2^27 - 1, M * K at most 2^40, and for the
  *    calls that run a GEMM (svdq_gemm_w4a4, svdq_linear_w4a4*,
  *    awq_linear_w4a16) at most 2^31 - 1 output tiles of 256 x 256
  *    (ceil(M / 256) * ceil(N / 256)); beyond them SVDQ_ERR_INVALID_ARG.

@@ -212,18 +212,18 @@ def test_gemm_calls_reject_too_many_output_tiles(lib):
     32-bit integers) is rejected before any HIP call (fake pointers are never
     touched); the largest legal M and N alone pass the size checks."""
     p = ctypes.c_void_p
-    big = 1 << 30
-    st = lib.svdq_gemm_w4a4(p(0x10000), p(0x20000), None, big, 64, big, 0, 0, p(0x30000),
+    big, bign = (1 << 27) - 1, (1 << 27) - 16          # N a multiple of 16
+    st = lib.svdq_gemm_w4a4(p(0x10000), p(0x20000), None, big, 64, bign, 0, 0, p(0x30000),
                             p(0x40000), None, None, None, None, 0, p(0x50000), 1, None)
     assert st == INVALID and "tiles" in svdq.svdq_last_error()
-    st = lib.svdq_linear_w4a4(p(0x10000), 1, big, 64, big, 0, 0, p(0x20000), None, None,
+    st = lib.svdq_linear_w4a4(p(0x10000), 1, big, 64, bign, 0, 0, p(0x20000), None, None,
                               p(0x40000), p(0x50000), None, None, None, 0, p(0x70000), 1,
                               p(0x100000), 1 << 40, None)
     assert st == INVALID and "tiles" in svdq.svdq_last_error()
-    st = lib.awq_linear_w4a16(p(0x10000), big, 64, big, 64, p(0x20000), p(0x30000),
+    st = lib.awq_linear_w4a16(p(0x10000), big, 64, bign, 64, p(0x20000), p(0x30000),
                               p(0x40000), None, p(0x50000), 1, None)
     assert st == INVALID and "tiles" in svdq.svdq_last_error()
-    # over 2^30 rows or columns: out of range
+    # 2^27 rows or columns: out of range
     st = lib.svdq_gemm_w4a4(p(0x10000), p(0x20000), None, big + 1, 64, 64, 0, 0, p(0x30000),
                             p(0x40000), None, None, None, None, 0, p(0x50000), 1, None)
     assert st == INVALID

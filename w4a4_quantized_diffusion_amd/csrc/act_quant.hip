@@ -867,18 +867,7 @@ struct RankDispatch {
   }
 };
 
-// compute units of the current device (cached per device; 0 if unknown)
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
+using svdq::cu_count;
 
 // Whether 8-row workgroups finish sooner than 16-row ones: with one
 // workgroup per CU, the time goes as (rounds of workgroups) x (rows each).

@@ -25,13 +25,26 @@ svdq_status check_launch(const char* what) {
   return SVDQ_OK;
 }
 
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace svdq
 
 using svdq::fail;
 
 namespace {
 
-constexpr int64_t MAX_DIM = int64_t(1) << 30;
+// every kernel forms row offsets within one K-group as 32-bit integers
+constexpr int64_t MAX_DIM = (int64_t(1) << 27) - 1;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -270,11 +270,12 @@ def svdq_fold_lora(layer, A, B, scale=1.0):
     patterns): rank becomes round_up(rank + r_lora, 16), lora_down / lora_up
     are new tensors, every other entry is shared with `layer`."""
     N, K, rank = layer["N"], layer["K"], layer["rank"]
+    ref = layer.get("wcodes", layer.get("lora_down"))
     for name, t in (("A", A), ("B", B)):
         if t.dtype not in (torch.bfloat16, torch.int16):
             raise TypeError(f"{name} must be bfloat16 (or its int16 bit patterns), got {t.dtype}")
-        if t.device != layer["wcodes"].device:
-            raise ValueError(f"{name} is on {t.device}, the layer on {layer['wcodes'].device}")
+        if ref is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the layer on {ref.device}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     A, B = _bf16_bits(A), _bf16_bits(B)
