@@ -176,6 +176,24 @@ def test_linear_deterministic_and_fully_written():
     assert torch.equal(y1, y2), "two runs differ"
 
 
+def test_bf16_output_is_rne_of_f32_output():
+    """The bf16 output is the round-to-nearest-even bf16 of the fp32 output
+    of the same call, bit for bit (the epilogue's conversion), also with the
+    outputs scaled into the subnormal range and up to about 2^100."""
+    s = synth.layer(300, 1024, 272, 32, seed=6, workload="attn")
+    lay = _oracle_layer(s["w"], s["x"], 32)
+    for scale in (1.0, 2.0 ** -128, 2.0 ** 100):
+        d = layer_to_device(dict(lay, sW=(lay["sW"] * np.float32(scale)).astype(np.float32),
+                                 lora_up=lay["lora_up"] * scale), 32, 272, 1024)
+        x = t_x(s["x"], True)
+        y32 = svdq.svdq_linear_w4a4(x, d, y_dtype=torch.float32)
+        y16 = svdq.svdq_linear_w4a4(x, d, y_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        f = y32.cpu().numpy()
+        assert np.all(np.isfinite(f))
+        assert np.array_equal(bf16_bits_np(y16), F.bf16_bits(f)), f"scale {scale}"
+
+
 def test_act_absmax_matches():
     s = synth.layer(333, 1024, 16, 0, seed=5, workload="attn")
     a = svdq.svdq_act_absmax(t_x(s["x"], True))
