@@ -209,12 +209,28 @@ __device__ __forceinline__ void unpack_smooth(const SmoothRaw& r, float (&s0)[8]
   }
 }
 
-// t = z fl32(1/s) lies within 2^-20 of fl32(z / s) for |z| <= 7 s; only a
-// t within 2^-19 of a half-integer can round differently from the quotient.
-// Given r = rne(|t|), |t| is that close to a half-integer exactly when it
-// lies at least 1/2 - 2^-19 from r (the difference is exact).
+// The INT4 group scale s = fl32(amax / 7) without a division: q0 = a c with
+// c = fl32(1/7), the remainder a - 7 q0 (exact in one fma) and one
+// correction step.  For every a in [2^-100, 2^100] and for 0 this equals the
+// correctly rounded quotient (all of them checked on the device); other
+// values (tiny, huge, inf, NaN) take the division.
+__device__ __forceinline__ float int4_scale(float a) {
+  const float c = 1.0f / 7.0f;
+  const float q0 = a * c;
+  float s = fmaf(fmaf(-q0, 7.0f, a), c, q0);
+  if (!(a <= 0x1p100f && (a >= 0x1p-100f || a == 0.0f))) s = a / 7.0f;
+  return s;
+}
+
+// The quotients z / s go through v_rcp_f32, within 1 ulp of 1/s for every
+// normal s (checked on the device), so t = z rcp(s) lies within 1.6 2^-20 of
+// fl32(z / s) for |z| <= amax <= 7 s (1 + 2^-23): only a t within 2^-19 of a
+// half-integer can round differently from the quotient.  Given r = rne(|t|),
+// |t| is that close to a half-integer exactly when it lies at least
+// 1/2 - 2^-19 from r (the difference is exact).
+constexpr float NEAR_HALF = 0.5f - 0x1p-19f;
 __device__ __forceinline__ bool near_half_r(float t, float r) {
-  return fabsf(r - fabsf(t)) >= 0.5f - 0x1p-19f;
+  return fabsf(r - fabsf(t)) >= NEAR_HALF;
 }
 
 // INT4 code of t (|t| < 7.5), given r = rne(|t|), as its 6-bit field of the
@@ -424,8 +440,8 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
     }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float s = amax / 7.0f;
-    const float inv = 1.0f / s;
+    const float s = int4_scale(amax);
+    const float inv = __builtin_amdgcn_rcpf(s);
     const bool fast = s >= 0x1p-126f;
     uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
     if (s > 0.f) {
@@ -433,16 +449,16 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_int4_kernel(
       // has one within 2^-19 of a half-integer (or a tiny scale) does the
       // wave take the exact divisions, for those values
       float t0[8], t1[8], r0[8], r1[8];
-      bool need = !fast;
+      float dev = 0.f;   // largest |r - |t|| of the lane
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         t0[j] = x0[j] * inv;
         t1[j] = x1[j] * inv;
         r0[j] = rintf(fabsf(t0[j]));
         r1[j] = rintf(fabsf(t1[j]));
-        need |= unsigned(near_half_r(t0[j], r0[j])) | unsigned(near_half_r(t1[j], r1[j]));
+        dev = fmaxf(dev, fmaxf(fabsf(r0[j] - fabsf(t0[j])), fabsf(r1[j] - fabsf(t1[j]))));
       }
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      if (__builtin_amdgcn_ballot_w64(!fast || dev >= NEAR_HALF) != 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (!fast || near_half_r(t0[j], r0[j])) {
@@ -750,20 +766,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 || RB > 2 ? 2 : 3) void act_quant_
       a = fmaxf(a, __shfl_xor(a, 8));
       a = fmaxf(a, __shfl_xor(a, 16));
       a = fmaxf(a, __shfl_xor(a, 32));
-      const float s = a / 7.0f;
-      const float inv = 1.0f / s;
+      const float s = int4_scale(a);
+      const float inv = __builtin_amdgcn_rcpf(s);
       const bool fast = s >= 0x1p-126f;
       uint32_t lo = 0, hi = 0;
       if (s > 0.f) {
         float tq[8], rq[8];
-        bool need = !fast;
+        float dev = 0.f;   // largest |r - |t|| of the lane
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           tq[j] = x[j] * inv;
           rq[j] = rintf(fabsf(tq[j]));
-          need |= near_half_r(tq[j], rq[j]);
+          dev = fmaxf(dev, fabsf(rq[j] - fabsf(tq[j])));
         }
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        if (__builtin_amdgcn_ballot_w64(!fast || dev >= NEAR_HALF) != 0) {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             if (!fast || near_half_r(tq[j], rq[j])) {

@@ -43,18 +43,20 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 }
 
 // 8 unsigned nibbles (one dword, even k low) -> 8 bf16 values (q - z) s in
-// k order, as 4 dwords.  zs = -z s (exact in fp32).
+// k order, as 4 dwords.  zs = -z s (exact in fp32).  A byte 0x0q read as
+// FP8-E4M3 is q 2^-9 for every q in 0..15 (a subnormal below 8, exponent
+// field 1 from 8 on), so the scaled conversion with the power of two 2^9
+// gives q exactly, two codes per instruction.
 __device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float zs) {
-  const uint32_t e = w & 0x0F0F0F0Fu, o = (w >> 4) & 0x0F0F0F0Fu;
-  // (byte i) -> float: the compiler selects v_cvt_f32_ubyte<i>
-  const float q0 = float(e & 0xFFu), q1 = float(o & 0xFFu);
-  const float q2 = float((e >> 8) & 0xFFu), q3 = float((o >> 8) & 0xFFu);
-  const float q4 = float((e >> 16) & 0xFFu), q5 = float((o >> 16) & 0xFFu);
-  const float q6 = float(e >> 24), q7 = float(o >> 24);
-  return make_uint4(pk_bf16(fmaf(q0, s, zs), fmaf(q1, s, zs)),
-                    pk_bf16(fmaf(q2, s, zs), fmaf(q3, s, zs)),
-                    pk_bf16(fmaf(q4, s, zs), fmaf(q5, s, zs)),
-                    pk_bf16(fmaf(q6, s, zs), fmaf(q7, s, zs)));
+  const int e = int(w & 0x0F0F0F0Fu), o = int((w >> 4) & 0x0F0F0F0Fu);
+  const f2_t q02 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, 512.0f, false);
+  const f2_t q46 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, 512.0f, true);
+  const f2_t q13 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(o, 512.0f, false);
+  const f2_t q57 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(o, 512.0f, true);
+  return make_uint4(pk_bf16(fmaf(q02.x, s, zs), fmaf(q13.x, s, zs)),
+                    pk_bf16(fmaf(q02.y, s, zs), fmaf(q13.y, s, zs)),
+                    pk_bf16(fmaf(q46.x, s, zs), fmaf(q57.x, s, zs)),
+                    pk_bf16(fmaf(q46.y, s, zs), fmaf(q57.y, s, zs)));
 }
 
 __device__ __forceinline__ void store_y(void* Y, bool ybf16, int64_t idx, float v) {
