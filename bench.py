@@ -293,11 +293,15 @@ def time_calls(fn, steps, warmup=3):
     return np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
 
 
-def time_loop(fn, steps, warmup=3):
-    """Average duration (seconds) of fn(i) issued back to back, HIP events
-    on the current stream around the whole loop.  For kernels of a few
-    microseconds an event pair around each call adds its own overhead; the
-    loop average is the rate at which the stream runs them."""
+GRAPH_CALLS = 50   # consecutive calls captured in one graph by time_loop
+TIMING_LOOP = f"HIP graph of {GRAPH_CALLS} consecutive calls, replayed; events around the replays"
+TIMING_LOOPS = TIMING_LOOP.replace("graph of", "graphs of")
+
+def time_eager(fn, steps, warmup=3):
+    """Average duration (seconds) of fn(i) issued back to back from Python,
+    HIP events on the current stream around the whole loop.  For kernels of
+    a few microseconds the host's issue rate can be the limit: time_loop
+    removes it."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -309,6 +313,37 @@ def time_loop(fn, steps, warmup=3):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e-3 / steps
+
+
+def time_loop(fn, steps, warmup=3):
+    """Average duration (seconds) of fn(i) on the GPU: calls i = 0 .. n-1
+    (n = min(steps, GRAPH_CALLS)) captured back to back in one HIP graph,
+    replayed until at least `steps` calls have run, HIP events on the
+    replay stream around the replays.  The calls and their inputs are the
+    same as when issued eagerly; the graph only takes the host's issue time
+    per call out of the measurement."""
+    import math
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    n = max(1, min(steps, GRAPH_CALLS))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    for _ in range(max(1, warmup // n)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(steps / n))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) * 1e-3 / (reps * n)
 
 
 def pct(a, q):
@@ -334,8 +369,9 @@ def gemm_bytes_int4(M, K, N, R):
 
 def int4_case(M, K, N, R, workload, steps, seed):
     """The INT4 layer at one DiT projection shape: weights quantized by the
-    library from a seeded synthetic weight, back-to-back loop averages of the
-    layer and of its two kernels after a warm-up loop of the same length."""
+    library from a seeded synthetic weight, the GPU time per call of the
+    layer and of its two kernels (time_loop) after a warm-up of the same
+    length."""
     import torch
     from w4a4_quantized_diffusion_amd import svdq, synth
     dev = torch.device("cuda:0")
@@ -357,7 +393,7 @@ def int4_case(M, K, N, R, workload, steps, seed):
     ops = 2.0 * M * N * K
     ab = act_bytes_int4(M, K, R)
     return {"workload": f"INT4 g64, rank {R}, M {M} x K {K} -> N {N}, bf16 in / bias / out",
-            "timing": "back-to-back loop averages",
+            "timing": TIMING_LOOPS,
             "linear_us": round(t_lin * 1e6, 2),
             "TOPS": round(ops / t_lin / 1e12, 1),
             "pct_of_int8_peak": round(100.0 * ops / t_lin / 1e12 / PEAK_INT8_TOPS, 2),
@@ -417,7 +453,7 @@ def other_paths(steps):
         "workload": "NVFP4 (E2M1 b16, E4M3 block scales), rank 32, M 4608 x K 3072 -> N 12288",
         "linear_us": round(t_lin_loop * 1e6, 2),
         "TOPS": round(ops / t_lin_loop / 1e12, 1),
-        "timing": "back-to-back loop averages",
+        "timing": TIMING_LOOPS,
         "gemm_nvfp4": {"avg_us": round(t_gem_loop * 1e6, 2),
                        "per_call_bracket_us": round(float(t_gem.mean()) * 1e6, 2),
                        "TFLOP/s": round(ops / t_gem_loop / 1e12, 1), "bound": "mfma (f16)",
@@ -425,7 +461,7 @@ def other_paths(steps):
                        "frac_fp4_peak": round(ops / t_gem_loop / 1e12 / PEAK_FP4_TFLOPS, 4)},
         "act_quant_nvfp4": {"avg_us": round(t_act_loop * 1e6, 2),
                             "per_call_bracket_us": round(float(t_act.mean()) * 1e6, 2),
-                            "timing": "back-to-back loop average",
+                            "timing": TIMING_LOOP,
                             "algorithmic_bytes": act_bytes,
                             "GB/s": round(act_bytes / t_act_loop / 1e9, 1),
                             "frac_hbm": round(act_bytes / t_act_loop / 1e9 / PEAK_HBM_GBS, 4)},
@@ -460,7 +496,7 @@ def other_paths(steps):
     res["int4_mlp_down_gelu"] = {
         "workload": "INT4 g64, rank 32, GELU fused into the activation pass, "
                     "M 4608 x K 12288 -> N 3072",
-        "timing": "back-to-back loop averages",
+        "timing": TIMING_LOOPS,
         "linear_us": round(t_lin_g * 1e6, 2),
         "TOPS": round(ops / t_lin_g / 1e12, 1),
         "pct_of_int8_peak": round(100.0 * ops / t_lin_g / 1e12 / PEAK_INT8_TOPS, 2),
@@ -478,14 +514,14 @@ def other_paths(steps):
     lay_l = svdq.svdq_fold_lora(lay, at, bt, 1.0)
     ws_l = torch.empty(svdq.svdq_workspace_bytes(M, K, lay_l["rank"]), dtype=torch.uint8,
                        device=dev)
-    t_fold = time_loop(lambda i: svdq.svdq_fold_lora(lay, at, bt, 1.0), 20, warmup=5)
+    t_fold = time_eager(lambda i: svdq.svdq_fold_lora(lay, at, bt, 1.0), 20, warmup=5)
     t_lin_l = time_loop(lambda i: svdq.svdq_linear_w4a4(x, lay_l, workspace=ws_l, Y=y), steps,
                         warmup=steps)
     fold_bytes = 2 * (R * K + N * R + RL * K + N * RL) + 2 * lay_l["rank"] * (K + N)
     res["int4_lora_folded"] = {
         "workload": f"INT4 g64, rank {R} + LoRA rank {RL} folded (rank {lay_l['rank']}), "
                     "M 4608 x K 12288 -> N 3072",
-        "timing": "back-to-back loop averages",
+        "timing": TIMING_LOOPS,
         "linear_us": round(t_lin_l * 1e6, 2),
         "linear_without_lora_us": round(t_lin_p * 1e6, 2),
         "fold_us": round(t_fold * 1e6, 2),
@@ -511,14 +547,14 @@ def other_paths(steps):
         y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
         nrot = copies if m <= 64 else 1
         fn = lambda i: svdq.awq_linear_w4a16(x, lays[i % nrot], Y=y)
-        # back-to-back loop average (at the weight-streaming sizes each call
-        # reads a different weight copy), after a warm-up loop
+        # GPU time per call (at the weight-streaming sizes each call reads a
+        # different weight copy), after a warm-up of the same length
         t = time_loop(fn, steps, warmup=steps)
         t_call = time_calls(fn, steps)
         byts = wbytes + m * K * 2 + m * N * 2
         flops = 2.0 * m * N * K
         r = {"avg_us": round(t * 1e6, 2), "per_call_bracket_us": round(float(t_call.mean()) * 1e6, 2),
-             "timing": "back-to-back loop average",
+             "timing": TIMING_LOOP,
              "algorithmic_bytes": byts,
              "GB/s": round(byts / t / 1e9, 1),
              "frac_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4),
@@ -647,6 +683,10 @@ def main():
                                                            Y=ys[i % args.nbuf]), args.steps)
     t_act_loop = time_loop(lambda i: svdq.svdq_act_quantize(xs[i % args.nbuf], layer, codes,
                                                             scales, lr), args.steps)
+    t_gemm_eager = time_eager(lambda i: svdq.svdq_gemm_w4a4(codes, scales, lr, layer, bias,
+                                                            Y=ys[i % args.nbuf]), args.steps)
+    t_act_eager = time_eager(lambda i: svdq.svdq_act_quantize(xs[i % args.nbuf], layer, codes,
+                                                              scales, lr), args.steps)
 
     ops = 2.0 * M * N * K
     value = ops / (ms_step * 1e-3) / 1e12
@@ -699,14 +739,16 @@ def main():
         },
         "kernels": {
             "act_quant_int4": {"avg_us": round(t_act_loop * 1e6, 3),
-                               "timing": "back-to-back loop average",
+                               "timing": TIMING_LOOP,
+                               "eager_loop_us": round(t_act_eager * 1e6, 3),
                                "per_call_bracket_p50_us": pct(t_act, 50),
                                "per_call_bracket_p95_us": pct(t_act, 95),
                                "algorithmic_bytes": act_bytes,
                                "GB/s": round(act_bytes / t_act_loop / 1e9, 1),
                                "frac_hbm": round(act_bytes / t_act_loop / 1e9 / PEAK_HBM_GBS, 4)},
             "gemm_int4": {"avg_us": round(t_gemm_loop * 1e6, 3),
-                          "timing": "back-to-back loop average",
+                          "timing": TIMING_LOOP,
+                          "eager_loop_us": round(t_gemm_eager * 1e6, 3),
                           "per_call_bracket_p50_us": pct(t_gemm, 50),
                           "per_call_bracket_p95_us": pct(t_gemm, 95),
                           "TOPS": round(gemm_tops, 2)},

@@ -97,6 +97,25 @@ def test_act_quant_degenerate_inputs():
     _check_act(x, lay, 0, bf16=False)
 
 
+@pytest.mark.parametrize("m", [100, 4096, 4608])
+def test_act_quant_scales_over_the_exponent_range(m):
+    """Group maxima spread over the whole fp32 range (each group's values a
+    normal sample times 2^e, e in [-135, 122], times a non-trivial fp32
+    smoothing factor): the scale fl32(amax / 7) and the codes, bit for bit,
+    from the smallest subnormal scales to the largest, including the ranges
+    below 2^-100 and above 2^100 where the kernels divide directly."""
+    k = 128
+    g = np.random.default_rng(17)
+    e = g.integers(-135, 123, size=(m, k // 64))
+    x = g.normal(size=(m, k)) * np.exp2(np.repeat(e, 64, axis=1))
+    x = x.astype(np.float32)
+    smooth = g.uniform(0.5, 2.0, size=k).astype(np.float32)
+    lay = dict(smooth=smooth, q=np.zeros((16, k), np.int8),
+               wcodes=np.zeros((16, k // 2), np.uint8), sW=np.ones((16, k // 64), np.float32),
+               lora_down=None, lora_up=None)
+    _check_act(x, lay, 0, bf16=False)
+
+
 def test_gemm_unit_scale_exact_integers():
     """rank 0, all scales 1, no bias, fp32 out: Y is the exact integer dot
     product of the codes (below 2^24, so exact in fp32)."""
