@@ -175,7 +175,11 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_kernel(
     const bool more = g + 1 < G;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      // the next substep's fragment reads are issued before this substep's
+      // MFMAs (the barrier keeps the scheduler from sinking them next to
+      // their use, where the LDS latency would stall the MFMAs)
       if (ks < 3) frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < RBL; ++i)
 #pragma unroll
