@@ -232,7 +232,10 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
         fa_raw = cur.code[aoff + 64 * (i + 1)];
         qa_nxt = cur.scale[wm * WM + (i + 1) * 32 + r32];
       }
+      // S goes to the matrix core first: the FMAs need it and both P, and
+      // the scheduler would otherwise issue it last, behind the two P
       S = __builtin_amdgcn_mfma_f32_32x32x1f32(qa, qb, zero32, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < CBL; ++j)
         P[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
