@@ -280,30 +280,63 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   if (g + 2 < G) step(g + 2, rg2, rg1);
   fmas(RBL - 1);
 
-  // ------------------------------------------------ epilogue: LR . up^T
+  // ------------------------------------------------ epilogue: bias, LR . up^T
+  // The bias and the LR / lora_up fragments of up to two rank steps are
+  // loaded at once, so the epilogue waits for one round trip per two rank
+  // steps instead of one per load.  Rows and columns past the matrix edge
+  // load the last row / column: they reach only accumulator rows and columns
+  // that are never stored.
+  float bv[CBL];
+#pragma unroll
+  for (int j = 0; j < CBL; ++j) {
+    const int64_t n = n0 + wn * WN + j * 32 + r32;
+    const int64_t nc = n < N ? n : N - 1;
+    bv[j] = bias ? (BBF16 ? load_bias<uint16_t>(bias, nc) : load_bias<float>(bias, nc)) : 0.f;
+  }
   if constexpr (RK > 0) {
     const int R = RK * 16;
+    constexpr int KB = RK < 2 ? RK : 2;      // rank steps per batch of loads
+    int64_t urow[CBL], lrow[RBL];
 #pragma unroll
-    for (int kk = 0; kk < RK; ++kk) {
-      const int kof = kk * 16 + h * 8;
-      v4i ub[CBL];
+    for (int j = 0; j < CBL; ++j) {
+      const int64_t nb = n0 + wn * WN + j * 32 + r32;
+      urow[j] = (nb < N ? nb : N - 1) * R;
+    }
 #pragma unroll
-      for (int j = 0; j < CBL; ++j) {
-        const int64_t nb = n0 + wn * WN + j * 32 + r32;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (nb < N) u = *reinterpret_cast<const uint4*>(up + nb * R + kof);
-        ub[j] = v4i{int(u.x), int(u.y), int(u.z), int(u.w)};
+    for (int i = 0; i < RBL; ++i) {
+      const int64_t ra = m0 + wm * WM + i * 32 + r32;
+      lrow[i] = (ra < M ? ra : M - 1) * R;
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < RK; k0 += KB) {
+      v4i ub[KB][CBL], la[KB][RBL];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (k0 + kb < RK) {
+          const int kof = (k0 + kb) * 16 + h * 8;
+#pragma unroll
+          for (int j = 0; j < CBL; ++j) {
+            const uint4 u = *reinterpret_cast<const uint4*>(up + urow[j] + kof);
+            ub[kb][j] = v4i{int(u.x), int(u.y), int(u.z), int(u.w)};
+          }
+#pragma unroll
+          for (int i = 0; i < RBL; ++i) {
+            const uint4 l = *reinterpret_cast<const uint4*>(LR + lrow[i] + kof);
+            la[kb][i] = v4i{int(l.x), int(l.y), int(l.z), int(l.w)};
+          }
+        }
       }
 #pragma unroll
-      for (int i = 0; i < RBL; ++i) {
-        const int64_t ra = m0 + wm * WM + i * 32 + r32;
-        uint4 la = make_uint4(0, 0, 0, 0);
-        if (ra < M) la = *reinterpret_cast<const uint4*>(LR + ra * R + kof);
-        const v4i lai = {int(la.x), int(la.y), int(la.z), int(la.w)};
+      for (int kb = 0; kb < KB; ++kb) {
+        if (k0 + kb < RK) {
 #pragma unroll
-        for (int j = 0; j < CBL; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(v8bf, lai), __builtin_bit_cast(v8bf, ub[j]), acc[i][j], 0, 0, 0);
+          for (int i = 0; i < RBL; ++i)
+#pragma unroll
+            for (int j = 0; j < CBL; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(v8bf, la[kb][i]), __builtin_bit_cast(v8bf, ub[kb][j]),
+                  acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
@@ -321,13 +354,6 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   Ring* const eb_ring = wave < 2 ? &rg0 : wave < 4 ? &rg1 : wave < 6 ? &rg2 : &rg3;
   float* const eb = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(eb_ring) +
                                              (wave & 1) * EBYTES);
-  float bv[CBL];
-#pragma unroll
-  for (int j = 0; j < CBL; ++j) {
-    const int64_t n = n0 + wn * WN + j * 32 + r32;
-    bv[j] = (bias && n < N) ? (BBF16 ? load_bias<uint16_t>(bias, n) : load_bias<float>(bias, n))
-                            : 0.f;
-  }
   store_wave_tile<RBL, CBL, YBF16>(acc, bv, eb, lane, m0 + wm * WM, n0 + wn * WN, M, N, Y);
 }
 
