@@ -349,6 +349,8 @@ __global__ __launch_bounds__(NT) void awq_gemm_kernel(
     auto sub = [&](auto KC) {
       constexpr int ks = decltype(KC)::value;
       if (ks < 3) frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      // keeps the next substep's fragment reads ahead of this substep's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < RBL; ++i)
 #pragma unroll
