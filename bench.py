@@ -294,6 +294,7 @@ def time_calls(fn, steps, warmup=3):
 
 
 GRAPH_CALLS = 50   # consecutive calls captured in one graph by time_loop
+KERNEL_CALLS = 200  # least number of launches behind each per-kernel average
 TIMING_LOOP = f"HIP graph of {GRAPH_CALLS} consecutive calls, replayed; events around the replays"
 TIMING_LOOPS = TIMING_LOOP.replace("graph of", "graphs of")
 
@@ -679,14 +680,17 @@ def main():
     torch.cuda.synchronize()
     t_act = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    # the per-kernel averages run at least KERNEL_CALLS launches whatever K
+    # is (a single graph replay of 20 launches varies by several percent)
+    kn = max(args.steps, KERNEL_CALLS)
     t_gemm_loop = time_loop(lambda i: svdq.svdq_gemm_w4a4(codes, scales, lr, layer, bias,
-                                                           Y=ys[i % args.nbuf]), args.steps)
+                                                           Y=ys[i % args.nbuf]), kn, warmup=kn)
     t_act_loop = time_loop(lambda i: svdq.svdq_act_quantize(xs[i % args.nbuf], layer, codes,
-                                                            scales, lr), args.steps)
+                                                            scales, lr), kn, warmup=kn)
     t_gemm_eager = time_eager(lambda i: svdq.svdq_gemm_w4a4(codes, scales, lr, layer, bias,
-                                                            Y=ys[i % args.nbuf]), args.steps)
+                                                            Y=ys[i % args.nbuf]), kn)
     t_act_eager = time_eager(lambda i: svdq.svdq_act_quantize(xs[i % args.nbuf], layer, codes,
-                                                              scales, lr), args.steps)
+                                                              scales, lr), kn)
 
     ops = 2.0 * M * N * K
     value = ops / (ms_step * 1e-3) / 1e12
