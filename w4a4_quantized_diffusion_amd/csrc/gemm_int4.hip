@@ -128,13 +128,10 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
   const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, r32 = lane & 31;
 
-  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
-  // give each XCD a contiguous run of tiles (M fastest) to share its L2.
+  // XCD-aware, L2-blocked tile order (tile_origin)
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int total = tiles_m * tiles_n;
-  int t = blockIdx.x;
-  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
-  const int64_t m0 = int64_t(t % tiles_m) * BM, n0 = int64_t(t / tiles_m) * BN;
+  int64_t m0, n0;
+  tile_origin(tiles_m, tiles_n, BM, BN, m0, n0);
   const int G = K / 64;
 
   // DMA role: wave w fills 16-byte slots 128 w .. 128 w + 127 (rows 64 w ..

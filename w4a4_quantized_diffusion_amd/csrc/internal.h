@@ -193,4 +193,23 @@ __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[RBL][CBL],
   }
 }
 
+// Tile order of the 256 x 256-tile GEMM kernels.  Workgroups are dealt
+// round-robin to the 8 XCDs, so each XCD first gets a contiguous run of tile
+// indices; the run is then laid over the tile grid in column groups of 8
+// tiles, M fastest inside a group across its 8 columns, so that the 32 tiles
+// one XCD runs at a time cover about 4 row tiles by 8 column tiles and their
+// A rows and W rows stay in that XCD's L2 (about a third less HBM traffic
+// than a whole column of row tiles at a time).
+__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int bm, int bn,
+                                            int64_t& m0, int64_t& n0) {
+  constexpr int GN = 8;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int grp = t / (GN * tiles_m), in = t - grp * (GN * tiles_m);
+  const int gn = min(GN, tiles_n - grp * GN);
+  m0 = int64_t(in / gn) * bm;
+  n0 = int64_t(grp * GN + in % gn) * bn;
+}
+
 }  // namespace svdq_dev
